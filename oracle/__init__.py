@@ -1,0 +1,163 @@
+"""fp64 CPU oracle for the fused gated activation (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+in ``mlp_gated_activation_amd`` and never imports it.
+
+The arithmetic lives in ``glu_oracle.c`` (plain scalar C, IEEE double, host
+libm).  This module only loads that library, marshals numpy arrays and
+applies the ``[gate | up]`` layout, which is pure slicing:
+
+* "Write a Triton SiLU-Mul (SwiGLU) Kernel" -- "Inputs the agent should
+  gather first", item 4, and "Correctness requirements": a fused
+  ``(rows, 2*I)`` tensor holds the gate ``a`` in its first ``I`` columns and
+  the up projection ``b`` in the last ``I``; the activation goes on ``a``.
+* "Kernel Profile: SwiGLU (Tier 1 -- Element-wise)" -- "Key Patterns": the
+  backward writes ``da, db`` over the saved ``a, b``; in the fused layout the
+  gradient is therefore ``dx = [da | db]``.
+
+All inputs are the exact values of the stored (already rounded) tensors,
+given as float64 arrays; all outputs are unrounded float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+KINDS = {"silu": 0, "gelu_erf": 1, "gelu_tanh": 2, "relu": 3}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "glu_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build_lib(force: bool = False) -> str:
+    """Compile glu_oracle.c with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+             "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"],
+            check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build_lib()
+        lib = ctypes.CDLL(_LIB)
+        d = ctypes.c_double
+        i64 = ctypes.c_int64
+        pd = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_act.argtypes = [ctypes.c_int, d]
+        lib.oracle_act.restype = d
+        lib.oracle_dact.argtypes = [ctypes.c_int, d]
+        lib.oracle_dact.restype = d
+        for name in ("oracle_act_n", "oracle_dact_n"):
+            getattr(lib, name).argtypes = [ctypes.c_int, i64, pd, pd]
+            getattr(lib, name).restype = None
+        lib.oracle_fwd.argtypes = [ctypes.c_int, i64, pd, pd, pd]
+        lib.oracle_fwd.restype = None
+        lib.oracle_bwd.argtypes = [ctypes.c_int, i64, pd, pd, pd, pd, pd]
+        lib.oracle_bwd.restype = None
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _kind(kind) -> int:
+    if isinstance(kind, str):
+        return KINDS[kind]
+    if int(kind) not in KINDS.values():
+        raise ValueError(f"unknown kind {kind!r}")
+    return int(kind)
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x: np.ndarray):
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads() -> int:
+    """OpenMP threads the element loops use."""
+    return int(_load().oracle_num_threads())
+
+
+def act1(kind, x: float) -> float:
+    """act(x) for one scalar."""
+    return float(_load().oracle_act(_kind(kind), float(x)))
+
+
+def dact1(kind, x: float) -> float:
+    """act'(x) for one scalar."""
+    return float(_load().oracle_dact(_kind(kind), float(x)))
+
+
+def act(kind, x) -> np.ndarray:
+    x = _f64(x)
+    out = np.empty_like(x)
+    _load().oracle_act_n(_kind(kind), x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def dact(kind, x) -> np.ndarray:
+    x = _f64(x)
+    out = np.empty_like(x)
+    _load().oracle_dact_n(_kind(kind), x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def fwd(kind, a, b) -> np.ndarray:
+    """y = act(a) * b for separate a, b of one shape."""
+    a = _f64(a)
+    b = _f64(b)
+    if a.shape != b.shape:
+        raise ValueError(f"a{a.shape} and b{b.shape} differ in shape")
+    y = np.empty_like(a)
+    _load().oracle_fwd(_kind(kind), a.size, _ptr(a), _ptr(b), _ptr(y))
+    return y
+
+
+def bwd(kind, a, b, dy):
+    """(da, db) = (dy * act'(a) * b, dy * act(a)) for separate a, b, dy."""
+    a = _f64(a)
+    b = _f64(b)
+    dy = _f64(dy)
+    if not (a.shape == b.shape == dy.shape):
+        raise ValueError("a, b and dy must share one shape")
+    da = np.empty_like(a)
+    db = np.empty_like(a)
+    _load().oracle_bwd(_kind(kind), a.size, _ptr(a), _ptr(b), _ptr(dy), _ptr(da), _ptr(db))
+    return da, db
+
+
+def split_gate_up(x) -> tuple[np.ndarray, np.ndarray]:
+    """[gate | up] layout: a = x[:, :I], b = x[:, I:] for x of shape (rows, 2I)."""
+    x = np.asarray(x)
+    if x.ndim != 2 or x.shape[1] % 2:
+        raise ValueError(f"fused input must be (rows, 2*I), got {x.shape}")
+    i = x.shape[1] // 2
+    return x[:, :i], x[:, i:]
+
+
+def fwd_gate_up(kind, x) -> np.ndarray:
+    """y = act(x[:, :I]) * x[:, I:]."""
+    a, b = split_gate_up(x)
+    return fwd(kind, a, b)
+
+
+def bwd_gate_up(kind, x, dy) -> np.ndarray:
+    """dx = [da | db] for the fused layout."""
+    a, b = split_gate_up(x)
+    da, db = bwd(kind, a, b, dy)
+    return np.concatenate([da, db], axis=1)

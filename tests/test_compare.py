@@ -1,0 +1,106 @@
+"""CPU tests of the output-ulp comparator and of the seeded input generators."""
+import numpy as np
+import pytest
+import torch
+
+from oracle.compare import FORMATS, compare, ulp
+from mlp_gated_activation_amd import inputs
+
+
+def test_ulp_values():
+    assert ulp(np.array([1.0]), FORMATS["bf16"])[0] == 2.0 ** -7
+    assert ulp(np.array([1.5]), FORMATS["fp16"])[0] == 2.0 ** -10
+    assert ulp(np.array([-3.0]), FORMATS["fp16"])[0] == 2.0 ** -9
+    # subnormal floor
+    assert ulp(np.array([0.0]), FORMATS["bf16"])[0] == 2.0 ** -133
+    assert ulp(np.array([0.0]), FORMATS["fp16"])[0] == 2.0 ** -24
+    assert ulp(np.array([1e-30]), FORMATS["fp16"])[0] == 2.0 ** -24
+
+
+def test_bf16_one_ulp_bound():
+    r = np.array([1.0 + 2.0 ** -9] * 3)
+    g = np.array([1.0, 1.0 + 2.0 ** -7, 1.0 + 2.0 ** -6])
+    rep = compare(g, r, "bf16")
+    assert rep.n_fail == 1 and rep.argmax == 2
+    assert rep.max_ulp == pytest.approx(1.75)
+
+
+def test_fp16_subnormal_floor():
+    r = np.array([3e-8, 3e-8, -1e-9])
+    g = np.array([0.0, 2 * 2.0 ** -24, -0.0])
+    rep = compare(g, r, "fp16")
+    assert rep.n_fail == 1 and rep.argmax == 1
+
+
+def test_overflow_and_nan():
+    r = np.array([70000.0, 65520.0, 65520.0, 70000.0, np.nan, 1.0, np.nan])
+    g = np.array([np.inf, np.inf, 65504.0, 65504.0, np.nan, np.nan, 0.0])
+    rep = compare(g, r, "fp16")
+    # fails: 65504 for 70000 (index 3), NaN for 1.0 (5), 0 for NaN (6)
+    assert rep.n_fail == 3
+    ok = [compare(g[i:i + 1], r[i:i + 1], "fp16").ok for i in range(len(r))]
+    assert ok == [True, True, True, False, True, False, False]
+
+
+def test_fp32_relative_bound():
+    r = np.array([1.0, 1.0, 0.0])
+    g = np.array([1.0 + 0.9e-6, 1.0 + 2e-6, 2.0 ** -149])
+    ok = [compare(g[i:i + 1], r[i:i + 1], "fp32").ok for i in range(3)]
+    assert ok == [True, False, True]
+
+
+def test_large_array_chunks_report_first_failure_class():
+    n = (1 << 22) + 5
+    r = np.ones(n)
+    g = np.ones(n)
+    g[-1] = 1.0 + 2.0 ** -5
+    rep = compare(g, r, "bf16")
+    assert rep.n_fail == 1 and rep.argmax == n - 1 and rep.max_ulp == pytest.approx(4.0)
+
+
+def test_inputs_are_deterministic_and_rounded():
+    a1, b1, d1 = inputs.separate(8, 40, "bf16", 2.0, seed=0)
+    a2, b2, d2 = inputs.separate(8, 40, "bf16", 2.0, seed=0)
+    assert all(torch.equal(u, v) for u, v in ((a1, a2), (b1, b2), (d1, d2)))
+    assert a1.dtype == torch.bfloat16 and a1.shape == (8, 40)
+    a3, _, _ = inputs.separate(8, 40, "bf16", 2.0, seed=1)
+    assert not torch.equal(a1, a3)
+    # rounding: the stored tensor equals the RNE cast of the fp32 draw
+    g = torch.Generator().manual_seed(0)
+    want = (torch.randn(8, 40, generator=g) * 2.0).to(torch.bfloat16)
+    assert torch.equal(a1, want)
+
+
+def test_input_distributions():
+    a, b, dy = inputs.separate(256, 1024, "fp32", 2.0)
+    assert abs(a.std().item() - 2.0) < 0.02 and abs(b.std().item() - 1.0) < 0.01
+    x, dy = inputs.gate_up(256, 512, "bf16", 1.5)
+    assert x.shape == (256, 1024) and dy.shape == (256, 512)
+    assert abs(x.float().std().item() - 1.5) < 0.02
+
+
+def test_stress_gate_values():
+    x, dy = inputs.gate_up_stress(512, 1000, "fp16")
+    a = x[:, :1000].float()
+    big = a.abs() >= 20
+    frac = big.float().mean().item()
+    assert 0.008 < frac < 0.012
+    assert a.abs().max().item() <= 80.0
+    assert (a[big] > 0).float().mean().item() == pytest.approx(0.5, abs=0.05)
+    assert x[:, 1000:].float().abs().max().item() < 10
+
+
+def test_all_bit_patterns():
+    for dt in ("bf16", "fp16"):
+        v = inputs.all_bit_patterns(dt)
+        assert v.numel() == 65536
+        bits = v.view(torch.int16).to(torch.int32) & 0xFFFF
+        assert torch.equal(torch.sort(bits).values, torch.arange(65536, dtype=torch.int32))
+
+
+def test_workload_table():
+    w = inputs.WORKLOADS["swiglu_bf16_4096x14336"]
+    assert (w.rows, w.cols, w.dtype, w.layout) == (4096, 14336, "bf16", "separate")
+    w4 = inputs.WORKLOADS["geglu_reglu_fp16_gateup_8191x18944"]
+    assert w4.rows == 8191 and w4.cols == 18944 and w4.stress
+    assert len([n for n in inputs.WORKLOADS if n.startswith("swiglu_bf16_4096x")]) == 7
