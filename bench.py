@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused gated activation on one MI355X.
+
+One step = one pass of the whole path over one batch: the SwiGLU forward
+y = silu(a) * b out of place, then the backward in place (da over a, db over
+b), bf16, a, b, dy of shape (4096, 14336).  Inputs are seeded synthetic data
+(a ~ N(0, 2^2), b, dy ~ N(0, 1), rounded to bf16), resident in HBM before the
+timed region.  Several buffer sets are rotated so consecutive steps touch
+disjoint memory (well over the last-level cache), i.e. the numbers are HBM
+numbers, not cache numbers.
+
+Metric: achieved HBM GB/s = algorithmic bytes / time, algorithmic bytes =
+forward 3*N*2 + backward 5*N*2 = 939,524,096 B per step (N = 4096*14336).
+
+Prints one JSON line (see the keys below).  `--gpus N` with N > 1 exits with
+a message: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for bf16 silu(a)*b fwd+bwd at 4096x14336"
+PEAK_HBM_GBS = 8000.0
+ROWS, COLS = 4096, 14336
+N = ROWS * COLS
+ES = 2
+FWD_BYTES = 3 * N * ES          # read a, b; write y
+BWD_BYTES = 5 * N * ES          # read a, b, dy; write da, db
+STEP_BYTES = FWD_BYTES + BWD_BYTES
+KERNEL_SOURCES = ["mlp_gated_activation_amd/csrc/glu_kernels.hip",
+                  "mlp_gated_activation_amd/csrc/glu_internal.h",
+                  "mlp_gated_activation_amd/csrc/glu_taylor.h"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_glu_swiglu_bf16_4096x14336.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per backward launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("bwd_traffic_bytes")
+
+
+def cpu_baseline(a, b, dy):
+    """The fp64 oracle, as it stands, on the same inputs: fwd then bwd over
+    the whole (4096, 14336) batch, repeated while under ~10 s; best time."""
+    import numpy as np
+    import oracle
+    fa = a.to(dtype=__import__("torch").float64).numpy()
+    fb = b.to(dtype=__import__("torch").float64).numpy()
+    fdy = dy.to(dtype=__import__("torch").float64).numpy()
+    oracle.fwd("silu", fa[:8], fb[:8])          # load/compile outside the timing
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.fwd("silu", fa, fb)
+        oracle.bwd("silu", fa, fb, fdy)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all > 10.0 or len(times) >= 5:
+            break
+    best = min(times)
+    del fa, fb, fdy
+    return {
+        "value": round(STEP_BYTES / best / 1e9, 3),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"full workload, fwd+bwd over {ROWS}x{COLS} (fp64 scalar C, OpenMP), best of {len(times)}",
+        "elements_per_s": round(N / best, 1),
+        "seconds_per_step": round(best, 4),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets (470 MB each)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-check", action="store_true", default=True)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported. The op shards with no communication (rows or matched column slices), "
+              "so one GPU's throughput is the per-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    from mlp_gated_activation_amd import build as _build
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    from mlp_gated_activation_amd import glu, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = inputs.WORKLOADS["swiglu_bf16_4096x14336"]
+    a_h, b_h, dy_h = w.make(seed=0)
+    sets = []
+    for _ in range(args.sets):
+        sets.append([a_h.to(dev), b_h.to(dev), dy_h.to(dev), torch.empty(ROWS, COLS, dtype=torch.bfloat16, device=dev)])
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        a, b, dy, y = sets[i % len(sets)]
+        glu.glu_fwd("silu", "separate", a, b, y)
+        glu.glu_bwd("silu", "separate", a, b, dy, inplace=True)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        a, b, dy, y = sets[i % len(sets)]
+        e0, e1, e2 = ev[i]
+        e0.record(stream)
+        glu.glu_fwd("silu", "separate", a, b, y)
+        e1.record(stream)
+        glu.glu_bwd("silu", "separate", a, b, dy, inplace=True)
+        e2.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    mean = lambda v: sum(v) / len(v)
+    med = lambda v: v[len(v) // 2]
+    ms_per_step = total_ms / args.steps
+    value = STEP_BYTES / (ms_per_step * 1e-3) / 1e9
+
+    # attainable reference: a plain device copy (1 read + 1 write) of the same bytes
+    copy = None
+    if args.copy_check:
+        src = torch.empty(2 * N * ES * 3 // 2, dtype=torch.uint8, device=dev)
+        dsts = [torch.empty_like(src) for _ in range(3)]
+        for d in dsts:
+            d.copy_(src)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record(stream)
+        reps = 30
+        for r in range(reps):
+            dsts[r % 3].copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = 2 * src.numel() / (c0.elapsed_time(c1) / reps * 1e-3) / 1e9
+        copy = round(copy_gbs, 1)
+        del src, dsts
+
+    bwd_avg = mean(bwd_ms)
+    achieved = BWD_BYTES / (bwd_avg * 1e-3) / 1e9
+    traffic = committed_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded a~N(0,4), b,dy~N(0,1) rounded to bf16; "
+                f"{args.sets} rotating buffer sets, {args.sets * 4 * N * ES / 1e9:.2f} GB)",
+        "config": {
+            "workload": "SwiGLU bf16 separate a,b,dy (4096, 14336): fwd out-of-place + bwd in place",
+            "rows": ROWS, "cols": COLS, "kind": "silu", "layout": "separate",
+            "bytes_per_step": STEP_BYTES, "math": "fp32 in registers, one RNE rounding per output",
+        },
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "kernels": {
+            "fwd": {"avg_us": round(1e3 * mean(fwd_ms), 2), "median_us": round(1e3 * med(fwd_ms), 2),
+                    "GBps": round(FWD_BYTES / (mean(fwd_ms) * 1e-3) / 1e9, 1), "bytes": FWD_BYTES},
+            "bwd": {"avg_us": round(1e3 * bwd_avg, 2), "median_us": round(1e3 * med(bwd_ms), 2),
+                    "GBps": round(achieved, 1), "bytes": BWD_BYTES},
+        },
+        "copy_GBps": copy,
+        "pct_of_copy": round(100 * value / copy, 2) if copy else None,
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "glu_kernel<bf16, silu, bwd, vec>",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    del sets
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(a_h, b_h, dy_h)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,354 @@
+// glu_api.cpp -- host side of the C ABI declared in include/glu.h:
+// argument validation (entirely before any HIP call), aliasing analysis,
+// and launch planning.
+//
+// Sources (page title -- section):
+//   [SWIGLU] "Write a Triton SiLU-Mul (SwiGLU) Kernel"
+//   [LIGER]  "Kernel Profile: SwiGLU (Tier 1 -- Element-wise)"
+#include "glu.h"
+
+#include <stdint.h>
+#include <string.h>
+
+#include "glu_internal.h"
+
+namespace {
+
+using glu::Args;
+
+// A strided operand: `rows` rows of `width` elements, `ld` elements apart,
+// starting at byte address `p`.
+struct Region {
+    uintptr_t p;
+    int64_t ld;
+    int64_t width;
+};
+
+// Byte extent [p, p + extent) of a region; false on int64 overflow.
+bool extent_bytes(int64_t rows, const Region &r, int esize, int64_t *out)
+{
+    int64_t span;
+    if (__builtin_mul_overflow(rows - 1, r.ld, &span))
+        return false;
+    if (__builtin_add_overflow(span, r.width, &span))
+        return false;
+    if (__builtin_mul_overflow(span, int64_t(esize), &span))
+        return false;
+    uintptr_t end;
+    if (__builtin_add_overflow(r.p, uintptr_t(span), &end))
+        return false;
+    *out = span;
+    return true;
+}
+
+int64_t floor_div(int64_t a, int64_t b)  // b > 0
+{
+    int64_t q = a / b;
+    return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+
+// True when some element of region x and some element of region y share a
+// byte.  Exact for equal strides; conservative (true) when the byte extents
+// intersect and the strides differ.
+bool overlaps(int64_t rows, const Region &x, const Region &y, int esize)
+{
+    int64_t ex = 0, ey = 0;
+    extent_bytes(rows, x, esize, &ex);
+    extent_bytes(rows, y, esize, &ey);
+    if (x.p + uintptr_t(ex) <= y.p || y.p + uintptr_t(ey) <= x.p)
+        return false;
+    if (x.ld != y.ld)
+        return true;
+    // Rows i of x and i + k of y overlap iff -wy < d + k*L < wx  (bytes),
+    // d = y.p - x.p, L = ld * esize.
+    const int64_t L = x.ld * esize;
+    const int64_t d = int64_t(y.p - x.p);
+    const int64_t wx = x.width * esize, wy = y.width * esize;
+    int64_t klo = floor_div(-wy - d, L) + 1;         // smallest k with d + kL > -wy
+    int64_t khi = -floor_div(-(wx - d), L) - 1;      // largest k with d + kL < wx
+    if (klo < -(rows - 1))
+        klo = -(rows - 1);
+    if (khi > rows - 1)
+        khi = rows - 1;
+    return klo <= khi;
+}
+
+bool same(const Region &x, const Region &y) { return x.p == y.p && x.ld == y.ld && x.width == y.width; }
+
+// An output may coincide exactly with an input, never partially.
+bool bad_alias(int64_t rows, const Region &out, const Region *ins, int nin, int esize)
+{
+    for (int i = 0; i < nin; ++i)
+        if (!same(out, ins[i]) && overlaps(rows, out, ins[i], esize))
+            return true;
+    return false;
+}
+
+bool aligned16(uintptr_t p) { return (p & 15u) == 0; }
+
+// Enqueue launches covering `rows` x `cols` elements.  When every operand is
+// a dense (ld == cols) matrix the rows are merged into one long row.
+glu_status enqueue(int dtype, int kind, bool bwd, int64_t rows, int64_t cols, Args a, bool vec,
+                   hipStream_t stream)
+{
+    const int es = glu::elem_size(dtype);
+    const int ve = vec ? glu::vec_elems(dtype) : 1;
+    const int nin = bwd ? 3 : 2;
+    const int nout = bwd ? 2 : 1;
+    const int64_t *lds[5] = {&a.ld_in0, &a.ld_in1, &a.ld_in2, &a.ld_out0, &a.ld_out1};
+    const bool used[5] = {true, true, nin == 3, true, nout == 2};
+    bool dense = true;
+    for (int i = 0; i < 5; ++i)
+        if (used[i] && *lds[i] != cols)
+            dense = false;
+    if (dense && rows > 1) {
+        cols *= rows;
+        rows = 1;
+    }
+    const int64_t upr = (cols + ve - 1) / ve;   // units per row
+    const void *ins[3] = {a.in0, a.in1, a.in2};
+    void *outs[2] = {a.out0, a.out1};
+
+    auto run = [&](int64_t r0, int64_t nrows, int64_t c0, int64_t ncols) -> glu_status {
+        Args p = a;
+        const int64_t u = (ncols + ve - 1) / ve;
+        for (int i = 0; i < nin; ++i)
+            (&p.in0)[i] = static_cast<const char *>(ins[i]) + (r0 * *lds[i] + c0) * es;
+        for (int i = 0; i < nout; ++i)
+            (&p.out0)[i] = static_cast<char *>(outs[i]) + (r0 * *lds[3 + i] + c0) * es;
+        p.units = uint32_t(nrows * u);
+        p.units_per_row = uint32_t(u);
+        p.cols = uint32_t(ncols);
+        p.row_div = glu::make_divider(uint32_t(u));
+        return glu::launch(dtype, kind, bwd, vec, p, stream) == hipSuccess ? GLU_OK : GLU_ERR_HIP;
+    };
+
+    const int64_t maxu = glu::kMaxUnitsPerLaunch;
+    if (upr <= maxu) {
+        const int64_t rows_per = maxu / upr;
+        for (int64_t r0 = 0; r0 < rows; r0 += rows_per) {
+            int64_t n = rows - r0 < rows_per ? rows - r0 : rows_per;
+            glu_status s = run(r0, n, 0, cols);
+            if (s != GLU_OK)
+                return s;
+        }
+    } else {
+        // a single row longer than one launch: split it into column chunks
+        const int64_t chunk = maxu * ve;
+        for (int64_t r0 = 0; r0 < rows; ++r0)
+            for (int64_t c0 = 0; c0 < cols; c0 += chunk) {
+                glu_status s = run(r0, 1, c0, cols - c0 < chunk ? cols - c0 : chunk);
+                if (s != GLU_OK)
+                    return s;
+            }
+    }
+    return GLU_OK;
+}
+
+bool valid_enums(int kind, int layout, int dtype)
+{
+    return kind >= GLU_SILU && kind <= GLU_RELU && layout >= GLU_SEPARATE && layout <= GLU_GATE_UP &&
+           dtype >= GLU_F32 && dtype <= GLU_BF16;
+}
+
+// Shared checks of the input side; fills the a and b regions.
+glu_status check_inputs(glu_layout layout, int es, int64_t rows, int64_t cols, void *a, int64_t lda,
+                        void *b, int64_t ldb, Region *ra, Region *rb)
+{
+    if (a == nullptr)
+        return GLU_ERR_NULL;
+    if (layout == GLU_SEPARATE) {
+        if (b == nullptr)
+            return GLU_ERR_NULL;
+        if (lda < cols || ldb < cols)
+            return GLU_ERR_STRIDE;
+        *ra = Region{uintptr_t(a), lda, cols};
+        *rb = Region{uintptr_t(b), ldb, cols};
+    } else {
+        if (b != nullptr)
+            return GLU_ERR_NULL;
+        int64_t two;
+        if (__builtin_mul_overflow(cols, int64_t(2), &two))
+            return GLU_ERR_SHAPE;
+        if (lda < two)
+            return GLU_ERR_STRIDE;
+        *ra = Region{uintptr_t(a), lda, cols};
+        *rb = Region{uintptr_t(a) + uintptr_t(cols) * es, lda, cols};
+        int64_t ext;
+        if (!extent_bytes(rows, Region{uintptr_t(a), lda, two}, es, &ext))
+            return GLU_ERR_SHAPE;
+    }
+    int64_t ext;
+    if (!extent_bytes(rows, *ra, es, &ext) || !extent_bytes(rows, *rb, es, &ext))
+        return GLU_ERR_SHAPE;
+    return GLU_OK;
+}
+
+bool vec_ok(const Region *r, int n, int es, int64_t rows)
+{
+    for (int i = 0; i < n; ++i) {
+        if (!aligned16(r[i].p))
+            return false;
+        if (rows > 1 && ((r[i].ld * es) & 15) != 0)
+            return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+glu_status glu_fwd(glu_kind kind, glu_layout layout, glu_dtype dtype, int64_t rows, int64_t cols, void *a,
+                   int64_t lda, void *b, int64_t ldb, void *y, int64_t ldy, int inplace, hipStream_t stream)
+{
+    if (!valid_enums(kind, layout, dtype))
+        return GLU_ERR_ENUM;
+    if (inplace != 0 && inplace != 1)
+        return GLU_ERR_INPLACE;
+    if (rows < 0 || cols < 0)
+        return GLU_ERR_SHAPE;
+    if (rows == 0 || cols == 0)
+        return GLU_OK;
+    if (rows > INT32_MAX)
+        return GLU_ERR_SHAPE;
+    const int es = glu::elem_size(dtype);
+    Region ra, rb;
+    glu_status s = check_inputs(layout, es, rows, cols, a, lda, b, ldb, &ra, &rb);
+    if (s != GLU_OK)
+        return s;
+    Region ry;
+    if (inplace) {
+        if (y != nullptr)
+            return GLU_ERR_INPLACE;
+        ry = rb;   // [SWIGLU] Inputs, item 7: y may overwrite b
+    } else {
+        if (y == nullptr)
+            return GLU_ERR_NULL;
+        if (ldy < cols)
+            return GLU_ERR_STRIDE;
+        ry = Region{uintptr_t(y), ldy, cols};
+        int64_t ext;
+        if (!extent_bytes(rows, ry, es, &ext))
+            return GLU_ERR_SHAPE;
+        const Region ins[2] = {ra, rb};
+        if (bad_alias(rows, ry, ins, 2, es))
+            return GLU_ERR_ALIAS;
+    }
+    const Region all[3] = {ra, rb, ry};
+    const bool vec = vec_ok(all, 3, es, rows);
+    Args p{};
+    p.in0 = reinterpret_cast<const void *>(ra.p);
+    p.in1 = reinterpret_cast<const void *>(rb.p);
+    p.in2 = nullptr;
+    p.out0 = reinterpret_cast<void *>(ry.p);
+    p.out1 = nullptr;
+    p.ld_in0 = ra.ld;
+    p.ld_in1 = rb.ld;
+    p.ld_in2 = 0;
+    p.ld_out0 = ry.ld;
+    p.ld_out1 = 0;
+    return enqueue(dtype, kind, false, rows, cols, p, vec, stream);
+}
+
+glu_status glu_bwd(glu_kind kind, glu_layout layout, glu_dtype dtype, int64_t rows, int64_t cols, void *a,
+                   int64_t lda, void *b, int64_t ldb, const void *dy, int64_t lddy, void *da, int64_t ldda,
+                   void *db, int64_t lddb, int inplace, hipStream_t stream)
+{
+    if (!valid_enums(kind, layout, dtype))
+        return GLU_ERR_ENUM;
+    if (inplace != 0 && inplace != 1)
+        return GLU_ERR_INPLACE;
+    if (rows < 0 || cols < 0)
+        return GLU_ERR_SHAPE;
+    if (rows == 0 || cols == 0)
+        return GLU_OK;
+    if (rows > INT32_MAX)
+        return GLU_ERR_SHAPE;
+    const int es = glu::elem_size(dtype);
+    Region ra, rb;
+    glu_status s = check_inputs(layout, es, rows, cols, a, lda, b, ldb, &ra, &rb);
+    if (s != GLU_OK)
+        return s;
+    if (dy == nullptr)
+        return GLU_ERR_NULL;
+    if (lddy < cols)
+        return GLU_ERR_STRIDE;
+    const Region rdy{uintptr_t(dy), lddy, cols};
+    int64_t ext;
+    if (!extent_bytes(rows, rdy, es, &ext))
+        return GLU_ERR_SHAPE;
+    Region rda, rdb;
+    if (inplace) {
+        // [LIGER] Key Patterns: gradients written over the saved a and b
+        if (da != nullptr || db != nullptr)
+            return GLU_ERR_INPLACE;
+        rda = ra;
+        rdb = rb;
+        // dy must not overlap the outputs unless it is exactly one of them
+        const Region outs[2] = {rda, rdb};
+        for (int i = 0; i < 2; ++i)
+            if (!same(outs[i], rdy) && overlaps(rows, outs[i], rdy, es))
+                return GLU_ERR_ALIAS;
+    } else {
+        if (da == nullptr)
+            return GLU_ERR_NULL;
+        if (layout == GLU_SEPARATE) {
+            if (db == nullptr)
+                return GLU_ERR_NULL;
+            if (ldda < cols || lddb < cols)
+                return GLU_ERR_STRIDE;
+            rda = Region{uintptr_t(da), ldda, cols};
+            rdb = Region{uintptr_t(db), lddb, cols};
+        } else {
+            if (db != nullptr)
+                return GLU_ERR_NULL;
+            if (ldda < 2 * cols)
+                return GLU_ERR_STRIDE;
+            rda = Region{uintptr_t(da), ldda, cols};
+            rdb = Region{uintptr_t(da) + uintptr_t(cols) * es, ldda, cols};
+            if (!extent_bytes(rows, Region{uintptr_t(da), ldda, 2 * cols}, es, &ext))
+                return GLU_ERR_SHAPE;
+        }
+        if (!extent_bytes(rows, rda, es, &ext) || !extent_bytes(rows, rdb, es, &ext))
+            return GLU_ERR_SHAPE;
+        const Region ins[3] = {ra, rb, rdy};
+        if (bad_alias(rows, rda, ins, 3, es) || bad_alias(rows, rdb, ins, 3, es))
+            return GLU_ERR_ALIAS;
+    }
+    if (overlaps(rows, rda, rdb, es))
+        return GLU_ERR_ALIAS;
+    const Region all[5] = {ra, rb, rdy, rda, rdb};
+    const bool vec = vec_ok(all, 5, es, rows);
+    Args p{};
+    p.in0 = reinterpret_cast<const void *>(ra.p);
+    p.in1 = reinterpret_cast<const void *>(rb.p);
+    p.in2 = reinterpret_cast<const void *>(rdy.p);
+    p.out0 = reinterpret_cast<void *>(rda.p);
+    p.out1 = reinterpret_cast<void *>(rdb.p);
+    p.ld_in0 = ra.ld;
+    p.ld_in1 = rb.ld;
+    p.ld_in2 = rdy.ld;
+    p.ld_out0 = rda.ld;
+    p.ld_out1 = rdb.ld;
+    return enqueue(dtype, kind, true, rows, cols, p, vec, stream);
+}
+
+const char *glu_status_string(glu_status status)
+{
+    switch (status) {
+    case GLU_OK: return "success";
+    case GLU_ERR_NULL: return "a required pointer is NULL, or a pointer that must be NULL is not";
+    case GLU_ERR_SHAPE: return "negative dimension, or the operand extent overflows";
+    case GLU_ERR_STRIDE: return "a row stride is smaller than the row width";
+    case GLU_ERR_ENUM: return "kind, layout or dtype out of range";
+    case GLU_ERR_ALIAS: return "an output partially overlaps an input or another output";
+    case GLU_ERR_INPLACE: return "inplace must be 0 or 1, and output pointers must be NULL when it is 1";
+    case GLU_ERR_HIP: return "the HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int glu_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// glu_internal.h -- the launch plan passed from the host API (glu_api.cpp)
+// to the kernels (glu_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace glu {
+
+// Launch shape.  A "unit" is one 16-byte vector of every stream (8 bf16/fp16
+// or 4 fp32 elements), or a single element on the unaligned path.  Each
+// thread owns GLU_UNROLL units, BLOCK apart, so every wave's accesses to a
+// stream are contiguous 1 KiB runs.
+#ifndef GLU_BLOCK
+#define GLU_BLOCK 256
+#endif
+#ifndef GLU_UNROLL
+#define GLU_UNROLL 2
+#endif
+
+// Largest unit count one launch covers; keeps every per-launch index below
+// 2^31, which the kernels' 32-bit unsigned division relies on.
+constexpr uint32_t kMaxUnitsPerLaunch = 1u << 30;
+
+// Division by a runtime constant d >= 1 for numerators n < 2^31:
+//   n / d == (umulhi(n, magic) + n) >> shift
+// with shift = ceil(log2 d) and magic = floor(2^32 * (2^shift - d) / d) + 1.
+struct Divider {
+    uint32_t magic;
+    uint32_t shift;
+};
+
+inline Divider make_divider(uint32_t d)
+{
+    uint32_t s = 0;
+    while (s < 32 && (uint64_t(1) << s) < d)
+        ++s;
+    uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
+    return Divider{uint32_t(m), s};
+}
+
+// Kernel arguments: one plan per launch.  Pointers are byte addresses of
+// element (0, 0) of each operand; row strides are in elements.
+struct Args {
+    const void *in0;   // a
+    const void *in1;   // b
+    const void *in2;   // dy (backward only)
+    void *out0;        // y (forward) or da (backward)
+    void *out1;        // db (backward only)
+    int64_t ld_in0, ld_in1, ld_in2, ld_out0, ld_out1;
+    uint32_t units;          // units in this launch (< 2^31)
+    uint32_t units_per_row;  // ceil(cols / elements per unit)
+    uint32_t cols;           // elements per row in this launch
+    Divider row_div;         // division by units_per_row
+};
+
+enum Dtype { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Enqueues one launch; returns the HIP status of hipLaunchKernel.
+hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args,
+                  hipStream_t stream);
+
+// Elements moved per unit on the vector path, by dtype.
+inline int vec_elems(int dtype) { return dtype == F32 ? 4 : 8; }
+inline int elem_size(int dtype) { return dtype == F32 ? 4 : 2; }
+
+}  // namespace glu

@@ -1,0 +1,402 @@
+// glu_kernels.hip -- gfx950 kernels for y = act(a) * b and its backward.
+//
+// Sources (page title -- section):
+//   [SWIGLU] "Write a Triton SiLU-Mul (SwiGLU) Kernel"
+//   [LIGER]  "Kernel Profile: SwiGLU (Tier 1 -- Element-wise)"
+//   [FUSED]  "Fused Kernels"
+//
+// The op is a pure elementwise stream: 2 loads + 1 store per element forward,
+// 3 loads + 2 stores backward, a handful of fp32 operations in between
+// ([SWIGLU] "Performance requirements": arithmetic intensity well under one
+// flop per byte).  So the design is all about HBM:
+//  - each lane moves whole 16-byte vectors of every stream (global_load_dwordx4
+//    / global_store_dwordx4), and a wave covers 1 KiB contiguous per stream;
+//  - all of a thread's loads are issued before any math, so GLU_UNROLL
+//    vectors per stream are in flight per lane;
+//  - loads and stores carry the non-temporal hint: nothing is reused;
+//  - rows are addressed through row strides with one multiply-high division
+//    per 16-byte unit, never a per-element divide ([SWIGLU] "Performance
+//    requirements", interleaved layout cost);
+//  - there is no LDS, no cross-lane traffic and no MFMA.
+// Math: bf16/fp16 are widened to fp32, fp32 to fp64; the result is rounded
+// once at the store ([SWIGLU] "Kernel design rules").
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "glu_internal.h"
+#include "glu_taylor.h"
+
+namespace glu {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+enum Kind { SILU = 0, GELU_ERF = 1, GELU_TANH = 2, RELU = 3 };
+
+// ---------------------------------------------------------------------------
+// Storage types: unpack a 16-byte vector to the math type, pack it back with
+// one round-to-nearest-even per element.
+//
+// word() copies a vector element into a scalar before any __builtin_bit_cast:
+// this clang miscompiles __builtin_bit_cast applied directly to an
+// ext_vector element (it reads element 0 for every index).
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t word(u32x4 v, int j)
+{
+    uint32_t w = v[j];
+    return w;
+}
+
+struct SBf16 {
+    using M = float;
+    static constexpr int VE = 8;
+    static constexpr int SIZE = 2;
+    static constexpr bool PATCH = false;
+    __device__ static void unpack(u32x4 v, float *x)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __builtin_bit_cast(float, word(v, j) << 16);
+            x[2 * j + 1] = __builtin_bit_cast(float, word(v, j) & 0xffff0000u);
+        }
+    }
+    __device__ static u32x4 pack(const float *y)
+    {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y[2 * j], y[2 * j + 1]}, bf16x2));
+        return v;
+    }
+    __device__ static float load1(const void *p)
+    {
+        return __builtin_bit_cast(float, uint32_t(*static_cast<const uint16_t *>(p)) << 16);
+    }
+    __device__ static void store1(void *p, float y) { *static_cast<__bf16 *>(p) = static_cast<__bf16>(y); }
+};
+
+struct SF16 {
+    using M = float;
+    static constexpr int VE = 8;
+    static constexpr int SIZE = 2;
+    static constexpr bool PATCH = true;   // fp16 inputs reach within 2e-5 of act''s root
+    __device__ static void unpack(u32x4 v, float *x)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x2 t = __builtin_convertvector(__builtin_bit_cast(f16x2, word(v, j)), f32x2);
+            x[2 * j] = t[0];
+            x[2 * j + 1] = t[1];
+        }
+    }
+    __device__ static u32x4 pack(const float *y)
+    {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y[2 * j], y[2 * j + 1]}, f16x2));
+        return v;
+    }
+    __device__ static float load1(const void *p) { return float(*static_cast<const _Float16 *>(p)); }
+    __device__ static void store1(void *p, float y) { *static_cast<_Float16 *>(p) = static_cast<_Float16>(y); }
+};
+
+struct SF32 {
+    using M = double;
+    static constexpr int VE = 4;
+    static constexpr int SIZE = 4;
+    static constexpr bool PATCH = false;
+    __device__ static void unpack(u32x4 v, double *x)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            x[j] = double(__builtin_bit_cast(float, word(v, j)));
+    }
+    __device__ static u32x4 pack(const double *y)
+    {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __builtin_bit_cast(uint32_t, float(y[j]));
+        return v;
+    }
+    __device__ static double load1(const void *p) { return double(*static_cast<const float *>(p)); }
+    __device__ static void store1(void *p, double y) { *static_cast<float *>(p) = float(y); }
+};
+
+// ---------------------------------------------------------------------------
+// Activations.  All sigmoids use e = exp(-|x|) so nothing overflows
+// ([SWIGLU] "Kernel design rules": stable sigmoid for very negative x):
+//   q = 1/(1+e);  sigmoid(x) = q (x >= 0) or e*q (x < 0).
+// Derivatives are arranged so the one cancellation left (near act''s
+// negative root) is a single well-conditioned sum.
+// ---------------------------------------------------------------------------
+__device__ inline float recip(float x) { return __builtin_amdgcn_rcpf(x); }   // x in [1, 2]
+__device__ inline double recip(double x) { return 1.0 / x; }
+__device__ inline float fabs_(float x) { return __builtin_fabsf(x); }
+__device__ inline double fabs_(double x) { return __builtin_fabs(x); }
+__device__ inline float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ inline double fma_(double a, double b, double c) { return __builtin_fma(a, b, c); }
+
+template <typename M> __device__ inline M ex(M x);
+template <> __device__ inline float ex<float>(float x) { return expf(x); }
+template <> __device__ inline double ex<double>(double x) { return exp(x); }
+template <typename M> __device__ inline M erfc_(M x);
+template <> __device__ inline float erfc_<float>(float x) { return erfcf(x); }
+template <> __device__ inline double erfc_<double>(double x) { return erfc(x); }
+
+constexpr double kInvSqrt2 = 0.70710678118654752440;      // [SWIGLU] reasoning step 7
+constexpr double kInvSqrt2Pi = 0.39894228040143267794;
+constexpr double kSqrt2OverPi = 0.79788456080286535588;   // [SWIGLU] failure modes
+constexpr double kTanhCubic = 0.044715;
+
+// Clamp for the tanh form's polynomial: beyond |x| = 16 its sigmoid is 0 or
+// 1 in fp32 (and its contribution below any fp32/bf16/fp16 subnormal), while
+// x^3 would overflow.  NaN passes through.
+template <typename M> __device__ inline M tanh_clamp(M x)
+{
+    return x > M(16) ? M(16) : (x < M(-16) ? M(-16) : x);
+}
+
+template <int KIND, typename M> __device__ inline M act(M x)
+{
+    if constexpr (KIND == SILU) {
+        // silu(x) = x * sigmoid(x): [SWIGLU] reasoning step 5; [LIGER] Forward Pass
+        M e = ex<M>(-fabs_(x));
+        M q = recip(M(1) + e);
+        return x * (x >= M(0) ? q : e * q);
+    } else if constexpr (KIND == GELU_ERF) {
+        // x * Phi(x), Phi(x) = erfc(-x/sqrt2)/2 (no 1+erf cancellation): reasoning step 7
+        return x * (M(0.5) * erfc_<M>(x * M(-kInvSqrt2)));
+    } else if constexpr (KIND == GELU_TANH) {
+        // 0.5*x*(1+tanh(u)) = x * sigmoid(2u), u = sqrt(2/pi)(x + 0.044715 x^3)
+        M xc = tanh_clamp(x);
+        M w = xc * fma_(M(2 * kSqrt2OverPi * kTanhCubic), xc * xc, M(2 * kSqrt2OverPi));
+        M e = ex<M>(-fabs_(w));
+        M q = recip(M(1) + e);
+        return x * (w >= M(0) ? q : e * q);
+    } else {
+        // relu, NaN-propagating: [SWIGLU] Purpose (ReGLU)
+        return x > M(0) ? x : (x != x ? x : M(0));
+    }
+}
+
+// Polynomial for act' near its root (fp16 only; see gen_taylor.py).
+template <int KIND> __device__ inline float taylor_patch(float x, float d)
+{
+    constexpr float R = GLU_TAYLOR_RADIUS;
+    float hi, lo;
+    float c[4];
+    if constexpr (KIND == SILU) {
+        hi = GLU_TAYLOR_SILU_X0_HI; lo = GLU_TAYLOR_SILU_X0_LO;
+        const float cc[GLU_TAYLOR_SILU_DEG] = GLU_TAYLOR_SILU_COEFFS;
+        for (int k = 0; k < 4; ++k) c[k] = cc[k];
+    } else if constexpr (KIND == GELU_ERF) {
+        hi = GLU_TAYLOR_GELU_ERF_X0_HI; lo = GLU_TAYLOR_GELU_ERF_X0_LO;
+        const float cc[GLU_TAYLOR_GELU_ERF_DEG] = GLU_TAYLOR_GELU_ERF_COEFFS;
+        for (int k = 0; k < 4; ++k) c[k] = cc[k];
+    } else {
+        hi = GLU_TAYLOR_GELU_TANH_X0_HI; lo = GLU_TAYLOR_GELU_TANH_X0_LO;
+        const float cc[GLU_TAYLOR_GELU_TANH_DEG] = GLU_TAYLOR_GELU_TANH_COEFFS;
+        for (int k = 0; k < 4; ++k) c[k] = cc[k];
+    }
+    float h = x - hi;                  // exact (Sterbenz) inside the zone
+    float t = h - lo;
+    float p = __builtin_fmaf(c[3], t, c[2]);
+    p = __builtin_fmaf(p, t, c[1]);
+    p = __builtin_fmaf(p, t, c[0]);
+    return __builtin_fabsf(h) < R ? p * t : d;
+}
+
+// f = act(x) and g = act'(x) together (backward).
+template <int KIND, bool PATCH, typename M> __device__ inline void act_grad(M x, M &f, M &g)
+{
+    if constexpr (KIND == SILU) {
+        // silu' = s*(1 + x*(1-s)): [SWIGLU] correctness requirements; [LIGER]
+        // Backward Pass.  With e = exp(-|x|), q = 1/(1+e):
+        //   x >= 0:  q^2 * ((1+e) + x*e)
+        //   x <  0:  e*q^2 * ((1+x) + e)   (the root's cancellation is this one sum)
+        M e = ex<M>(-fabs_(x));
+        M q = recip(M(1) + e);
+        M q2 = q * q;
+        bool pos = x >= M(0);
+        f = x * (pos ? q : e * q);
+        g = pos ? q2 * fma_(x, e, M(1) + e) : (e * q2) * ((M(1) + x) + e);
+    } else if constexpr (KIND == GELU_ERF) {
+        // d/dx [x Phi(x)] = Phi(x) + x phi(x)
+        M Phi = M(0.5) * erfc_<M>(x * M(-kInvSqrt2));
+        M phi = ex<M>(M(-0.5) * x * x) * M(kInvSqrt2Pi);
+        f = x * Phi;
+        g = fma_(x, phi, Phi);
+    } else if constexpr (KIND == GELU_TANH) {
+        // w = 2u, v = 2x u'; sigmoid(w) (1 + v sigmoid(-w)):
+        //   w >= 0:  q^2 * ((1+e) + v*e)
+        //   w <  0:  e*q^2 * ((1+e) + v)
+        M xc = tanh_clamp(x);
+        M x2 = xc * xc;
+        M w = xc * fma_(M(2 * kSqrt2OverPi * kTanhCubic), x2, M(2 * kSqrt2OverPi));
+        M v = xc * fma_(M(6 * kSqrt2OverPi * kTanhCubic), x2, M(2 * kSqrt2OverPi));
+        M e = ex<M>(-fabs_(w));
+        M q = recip(M(1) + e);
+        M q2 = q * q;
+        bool pos = w >= M(0);
+        f = x * (pos ? q : e * q);
+        g = pos ? q2 * fma_(v, e, M(1) + e) : (e * q2) * ((M(1) + e) + v);
+        if (x != x)
+            g = x;
+    } else {
+        f = x > M(0) ? x : (x != x ? x : M(0));
+        g = x > M(0) ? M(1) : (x != x ? x : M(0));
+    }
+    if constexpr (PATCH && KIND != RELU)
+        g = taylor_patch<KIND>(x, g);
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.  Unit u of the launch covers row r = u / units_per_row and
+// columns [j*VE, min(j*VE + VE, cols)), j = u - r*units_per_row.  A unit
+// that reaches past the row end (cols not a multiple of VE) is handled
+// element by element; no access ever leaves [0, cols) of a row
+// ([SWIGLU] "Kernel design rules": always mask the tail).
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ inline u32x4 ldv(const void *base, int64_t off_elems)
+{
+    return __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4 *>(static_cast<const char *>(base) + off_elems * T::SIZE));
+}
+
+template <typename T>
+__device__ inline void stv(void *base, int64_t off_elems, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(static_cast<char *>(base) + off_elems * T::SIZE));
+}
+
+__device__ inline const void *at(const void *base, int64_t off, int size)
+{
+    return static_cast<const char *>(base) + off * size;
+}
+__device__ inline void *at(void *base, int64_t off, int size) { return static_cast<char *>(base) + off * size; }
+
+template <typename T, int KIND, bool BWD, bool VEC>
+__global__ void __launch_bounds__(GLU_BLOCK) glu_kernel(const Args p)
+{
+    using M = typename T::M;
+    constexpr int VE = VEC ? T::VE : 1;
+    constexpr int U = GLU_UNROLL;
+
+    const uint32_t first = blockIdx.x * uint32_t(GLU_BLOCK * U) + threadIdx.x;
+
+    uint32_t row[U], col[U];
+    bool live[U], full[U];
+    u32x4 va[U], vb[U], vd[U];
+
+    // Phase 1: locate every unit and issue all full-vector loads.
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        uint32_t u = first + uint32_t(k * GLU_BLOCK);
+        live[k] = u < p.units;
+        uint32_t r = (__umulhi(u, p.row_div.magic) + u) >> p.row_div.shift;
+        row[k] = r;
+        col[k] = (u - r * p.units_per_row) * uint32_t(VE);
+        full[k] = live[k] && (col[k] + uint32_t(VE) <= p.cols);
+        if constexpr (VEC) {
+            if (full[k]) {
+                va[k] = ldv<T>(p.in0, int64_t(r) * p.ld_in0 + col[k]);
+                vb[k] = ldv<T>(p.in1, int64_t(r) * p.ld_in1 + col[k]);
+                if constexpr (BWD)
+                    vd[k] = ldv<T>(p.in2, int64_t(r) * p.ld_in2 + col[k]);
+            }
+        }
+    }
+
+    // Phase 2: compute and store.
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        if (!live[k])
+            continue;
+        const int64_t r = row[k];
+        if (VEC && full[k]) {
+            M a[T::VE], b[T::VE], o0[T::VE];
+            T::unpack(va[k], a);
+            T::unpack(vb[k], b);
+            if constexpr (!BWD) {
+#pragma unroll
+                for (int e = 0; e < T::VE; ++e)
+                    o0[e] = act<KIND, M>(a[e]) * b[e];
+                stv<T>(p.out0, r * p.ld_out0 + col[k], T::pack(o0));
+            } else {
+                M dy[T::VE], o1[T::VE];
+                T::unpack(vd[k], dy);
+#pragma unroll
+                for (int e = 0; e < T::VE; ++e) {
+                    M f, g;
+                    act_grad<KIND, T::PATCH, M>(a[e], f, g);
+                    o0[e] = (dy[e] * g) * b[e];
+                    o1[e] = dy[e] * f;
+                }
+                stv<T>(p.out0, r * p.ld_out0 + col[k], T::pack(o0));
+                stv<T>(p.out1, r * p.ld_out1 + col[k], T::pack(o1));
+            }
+        } else {
+            // element path: unaligned data, or the ragged end of a row
+            const uint32_t n = p.cols - col[k] < uint32_t(VE) ? p.cols - col[k] : uint32_t(VE);
+            for (uint32_t e = 0; e < n; ++e) {
+                const int64_t c = int64_t(col[k]) + e;
+                M a = T::load1(at(p.in0, r * p.ld_in0 + c, T::SIZE));
+                M b = T::load1(at(p.in1, r * p.ld_in1 + c, T::SIZE));
+                if constexpr (!BWD) {
+                    T::store1(at(p.out0, r * p.ld_out0 + c, T::SIZE), act<KIND, M>(a) * b);
+                } else {
+                    M dy = T::load1(at(p.in2, r * p.ld_in2 + c, T::SIZE));
+                    M f, g;
+                    act_grad<KIND, T::PATCH, M>(a, f, g);
+                    T::store1(at(p.out0, r * p.ld_out0 + c, T::SIZE), (dy * g) * b);
+                    T::store1(at(p.out1, r * p.ld_out1 + c, T::SIZE), dy * f);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch table: [dtype][kind][backward][vec].
+// ---------------------------------------------------------------------------
+typedef void (*KernelFn)(const Args);
+
+template <typename T, int KIND, bool BWD>
+constexpr KernelFn pick(bool vec)
+{
+    return vec ? &glu_kernel<T, KIND, BWD, true> : &glu_kernel<T, KIND, BWD, false>;
+}
+
+template <typename T>
+KernelFn pick_kind(int kind, bool bwd, bool vec)
+{
+    switch (kind) {
+    case SILU: return bwd ? pick<T, SILU, true>(vec) : pick<T, SILU, false>(vec);
+    case GELU_ERF: return bwd ? pick<T, GELU_ERF, true>(vec) : pick<T, GELU_ERF, false>(vec);
+    case GELU_TANH: return bwd ? pick<T, GELU_TANH, true>(vec) : pick<T, GELU_TANH, false>(vec);
+    default: return bwd ? pick<T, RELU, true>(vec) : pick<T, RELU, false>(vec);
+    }
+}
+
+}  // namespace
+
+hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args, hipStream_t stream)
+{
+    KernelFn fn = dtype == F32 ? pick_kind<SF32>(kind, backward, vec)
+                : dtype == F16 ? pick_kind<SF16>(kind, backward, vec)
+                               : pick_kind<SBf16>(kind, backward, vec);
+    const uint32_t per_block = uint32_t(GLU_BLOCK) * GLU_UNROLL;
+    dim3 grid((args.units + per_block - 1) / per_block);
+    dim3 block(GLU_BLOCK);
+    Args copy = args;
+    void *kargs[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block, kargs, 0, stream);
+}
+
+}  // namespace glu

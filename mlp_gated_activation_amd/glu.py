@@ -1,0 +1,223 @@
+"""Thin Python binding of the C ABI in include/glu.h (libglu.so).
+
+Argument marshalling only: shapes, row strides, dtype codes, device pointers
+and the current HIP stream go to ``glu_fwd`` / ``glu_bwd``; every element of
+the result is computed by the library's gfx950 kernels.  PyTorch supplies the
+device memory and the stream.  Importing this module loads the library and
+raises ImportError if it has not been built (there is no fallback).
+
+Tensors: the activation dimension is the last one and must be contiguous
+(column stride 1); leading dimensions are merged into rows, which must be
+possible without a copy ("Write a Triton SiLU-Mul (SwiGLU) Kernel",
+"Common failure modes": never silently read a transposed view).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libglu.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                      "`python -m mlp_gated_activation_amd.build` (or __graft_entry__.build())")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_lib.glu_fwd.argtypes = [_i, _i, _i, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i, _p]
+_lib.glu_fwd.restype = _i
+_lib.glu_bwd.argtypes = [_i, _i, _i, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i, _p]
+_lib.glu_bwd.restype = _i
+_lib.glu_status_string.argtypes = [_i]
+_lib.glu_status_string.restype = ctypes.c_char_p
+_lib.glu_version.argtypes = []
+_lib.glu_version.restype = _i
+
+KINDS = {"silu": 0, "gelu_erf": 1, "gelu_tanh": 2, "relu": 3}
+LAYOUTS = {"separate": 0, "gate_up": 1}
+DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+STATUS = {0: "GLU_OK", 1: "GLU_ERR_NULL", 2: "GLU_ERR_SHAPE", 3: "GLU_ERR_STRIDE", 4: "GLU_ERR_ENUM",
+          5: "GLU_ERR_ALIAS", 6: "GLU_ERR_INPLACE", 7: "GLU_ERR_HIP"}
+
+
+class GluError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.glu_status_string(status).decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def version() -> int:
+    return int(_lib.glu_version())
+
+
+def status_string(status: int) -> str:
+    return _lib.glu_status_string(status).decode()
+
+
+def _code(table, key, what):
+    try:
+        return table[key]
+    except KeyError:
+        raise ValueError(f"unknown {what} {key!r}; expected one of {list(table)}") from None
+
+
+def _rows(t: torch.Tensor, name: str) -> torch.Tensor:
+    """View t as (rows, last) without copying."""
+    if t.dim() == 0:
+        raise ValueError(f"{name} must have at least one dimension")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous (stride 1), got {t.stride()}")
+    try:
+        return t.view(-1, t.shape[-1]) if t.dim() != 2 else t
+    except RuntimeError as e:
+        raise ValueError(f"{name}: leading dimensions cannot be merged without a copy") from e
+
+
+def _ld(t2: torch.Tensor) -> int:
+    return int(t2.stride(0)) if t2.shape[0] > 1 else int(t2.shape[1])
+
+
+def _check(tensors, dtype, device):
+    for name, t in tensors:
+        if t is None:
+            continue
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def glu_fwd(kind: str, layout: str, a: torch.Tensor, b: torch.Tensor | None = None,
+            y: torch.Tensor | None = None, inplace: bool = False, stream=None) -> torch.Tensor:
+    """y = act(a) * b.  layout "separate": a, b of shape (..., I).
+    layout "gate_up": a is x of shape (..., 2I), b is None.
+    inplace: the result overwrites b (separate) or x[..., I:] (gate_up) and
+    that tensor (view) is returned; otherwise y (allocated if None) is."""
+    k = _code(KINDS, kind, "kind")
+    lay = _code(LAYOUTS, layout, "layout")
+    dt = _code(DTYPES, a.dtype, "dtype")
+    if a.device.type != "cuda":
+        raise ValueError("tensors must be on a ROCm (cuda) device")
+    a2 = _rows(a, "a")
+    if lay == 0:
+        if b is None:
+            raise ValueError("layout 'separate' needs b")
+        if b.shape != a.shape:
+            raise ValueError(f"a{tuple(a.shape)} and b{tuple(b.shape)} differ in shape")
+        cols = a.shape[-1]
+        out_shape = a.shape
+        b2 = _rows(b, "b")
+    else:
+        if b is not None:
+            raise ValueError("layout 'gate_up' takes x as a and no b")
+        if a.shape[-1] % 2:
+            raise ValueError(f"gate_up input width {a.shape[-1]} is odd")
+        cols = a.shape[-1] // 2
+        out_shape = a.shape[:-1] + (cols,)
+        b2 = None
+    if inplace:
+        if y is not None:
+            raise ValueError("inplace=True writes over b; do not pass y")
+        out = b if lay == 0 else a[..., cols:]
+        y2 = None
+    else:
+        if y is None:
+            y = torch.empty(out_shape, dtype=a.dtype, device=a.device)
+        if tuple(y.shape) != tuple(out_shape):
+            raise ValueError(f"y has shape {tuple(y.shape)}, expected {tuple(out_shape)}")
+        out = y
+        y2 = _rows(y, "y")
+    _check([("b", b), ("y", y)], a.dtype, a.device)
+    rows = a2.shape[0]
+    with torch.cuda.device(a.device):
+        st = _lib.glu_fwd(k, lay, dt, rows, cols,
+                          _ptr(a2), _ld(a2),
+                          _ptr(b2), _ld(b2) if b2 is not None else 0,
+                          _ptr(y2), _ld(y2) if y2 is not None else 0,
+                          1 if inplace else 0, _stream(a.device, stream))
+    if st != 0:
+        raise GluError(st, "glu_fwd")
+    return out
+
+
+def glu_bwd(kind: str, layout: str, a: torch.Tensor, b: torch.Tensor | None, dy: torch.Tensor,
+            da: torch.Tensor | None = None, db: torch.Tensor | None = None, inplace: bool = True,
+            stream=None):
+    """da = dy * act'(a) * b, db = dy * act(a).
+    separate: returns (da, db); with inplace they are a and b themselves.
+    gate_up: a is x (..., 2I), b is None; returns dx = [da | db] of x's shape
+    (x itself when inplace; otherwise `da` is dx, allocated if None)."""
+    k = _code(KINDS, kind, "kind")
+    lay = _code(LAYOUTS, layout, "layout")
+    dt = _code(DTYPES, a.dtype, "dtype")
+    if a.device.type != "cuda":
+        raise ValueError("tensors must be on a ROCm (cuda) device")
+    a2 = _rows(a, "a")
+    if lay == 0:
+        if b is None or b.shape != a.shape:
+            raise ValueError("layout 'separate' needs b of a's shape")
+        cols = a.shape[-1]
+        b2 = _rows(b, "b")
+        g_shape = a.shape
+    else:
+        if b is not None:
+            raise ValueError("layout 'gate_up' takes x as a and no b")
+        if a.shape[-1] % 2:
+            raise ValueError(f"gate_up input width {a.shape[-1]} is odd")
+        cols = a.shape[-1] // 2
+        b2 = None
+        g_shape = a.shape[:-1] + (cols,)
+    if tuple(dy.shape) != tuple(g_shape):
+        raise ValueError(f"dy has shape {tuple(dy.shape)}, expected {tuple(g_shape)}")
+    dy2 = _rows(dy, "dy")
+    if inplace:
+        if da is not None or db is not None:
+            raise ValueError("inplace=True writes over a and b; do not pass da/db")
+        da2 = db2 = None
+        result = (a, b) if lay == 0 else a
+    else:
+        if lay == 0:
+            da = torch.empty_like(a) if da is None else da
+            db = torch.empty_like(a) if db is None else db
+            if da.shape != a.shape or db.shape != a.shape:
+                raise ValueError("da and db must have a's shape")
+            da2, db2 = _rows(da, "da"), _rows(db, "db")
+            result = (da, db)
+        else:
+            if db is not None:
+                raise ValueError("layout 'gate_up' writes dx through da; db must be None")
+            da = torch.empty_like(a) if da is None else da
+            if da.shape != a.shape:
+                raise ValueError("dx must have x's shape")
+            da2, db2 = _rows(da, "dx"), None
+            result = da
+    _check([("b", b), ("dy", dy), ("da", da), ("db", db)], a.dtype, a.device)
+    rows = a2.shape[0]
+    with torch.cuda.device(a.device):
+        st = _lib.glu_bwd(k, lay, dt, rows, cols,
+                          _ptr(a2), _ld(a2),
+                          _ptr(b2), _ld(b2) if b2 is not None else 0,
+                          _ptr(dy2), _ld(dy2),
+                          _ptr(da2), _ld(da2) if da2 is not None else 0,
+                          _ptr(db2), _ld(db2) if db2 is not None else 0,
+                          1 if inplace else 0, _stream(a.device, stream))
+    if st != 0:
+        raise GluError(st, "glu_bwd")
+    return result

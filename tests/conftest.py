@@ -8,3 +8,10 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def ensure_built():
+    """Build libglu.so only if it is not there yet (the tests never rebuild)."""
+    from mlp_gated_activation_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()

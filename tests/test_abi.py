@@ -1,0 +1,165 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports exactly what
+include/glu.h declares, and rejects every invalid argument combination on
+the host before any HIP call (nothing here launches a kernel)."""
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "glu.h")
+CSRC = os.path.join(ROOT, "mlp_gated_activation_amd", "csrc")
+
+from conftest import ensure_built
+
+ensure_built()
+from mlp_gated_activation_amd import glu  # noqa: E402
+lib = glu._lib
+
+OK, NULL, SHAPE, STRIDE, ENUM, ALIAS, INPLACE, HIP = range(8)
+P = 0x7f0000000000          # fake device addresses: validation never dereferences them
+S, GU = 0, 1
+F32, F16, BF16 = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"GLU_API\s+[\w\s\*]+?\b(glu_\w+)\s*\(", text)
+
+
+def test_header_declarations_are_exported():
+    names = declared_functions()
+    assert set(names) == {"glu_fwd", "glu_bwd", "glu_status_string", "glu_version"}
+    nm = subprocess.run(["nm", "-D", "--defined-only", glu.library_path()],
+                        capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in nm.splitlines() if " T " in l}
+    assert exported == set(names), exported
+
+
+def test_version_and_status_strings():
+    assert glu.version() >> 16 == 1
+    for s in range(8):
+        assert len(glu.status_string(s)) > 5
+    assert glu.status_string(99) == "unknown status"
+
+
+def fwd(kind=0, layout=S, dtype=BF16, rows=4, cols=64, a=P, lda=64, b=P + (1 << 20), ldb=64,
+        y=P + (2 << 20), ldy=64, inplace=0):
+    return lib.glu_fwd(kind, layout, dtype, rows, cols, a, lda, b, ldb, y, ldy, inplace, None)
+
+
+def bwd(kind=0, layout=S, dtype=BF16, rows=4, cols=64, a=P, lda=64, b=P + (1 << 20), ldb=64,
+        dy=P + (2 << 20), lddy=64, da=P + (3 << 20), ldda=64, db=P + (4 << 20), lddb=64, inplace=0):
+    return lib.glu_bwd(kind, layout, dtype, rows, cols, a, lda, b, ldb, dy, lddy, da, ldda, db, lddb,
+                       inplace, None)
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(kind=4), ENUM), (dict(kind=-1), ENUM), (dict(layout=2), ENUM), (dict(dtype=3), ENUM),
+    (dict(inplace=2), INPLACE), (dict(inplace=-1), INPLACE),
+    (dict(rows=-1), SHAPE), (dict(cols=-5), SHAPE), (dict(rows=1 << 31), SHAPE),
+    (dict(rows=0, a=None, b=None, y=None), OK), (dict(cols=0, a=None, b=None, y=None), OK),
+    (dict(a=None), NULL), (dict(b=None), NULL), (dict(y=None), NULL),
+    (dict(layout=GU, b=P + (1 << 20), lda=128), NULL),          # gate_up takes no b
+    (dict(lda=63), STRIDE), (dict(ldb=10), STRIDE), (dict(ldy=0), STRIDE),
+    (dict(layout=GU, b=None, lda=127), STRIDE),                  # x needs 2*cols
+    (dict(inplace=1), INPLACE),                                  # y given with inplace
+    (dict(rows=1 << 30, lda=1 << 40), SHAPE),                    # extent overflows int64
+    (dict(cols=1 << 62, lda=1 << 62, ldb=1 << 62, ldy=1 << 62, rows=2), SHAPE),
+    (dict(y=P + 2 * 2), ALIAS),                                  # y straddles a's rows
+    (dict(y=P + (1 << 20) + 2 * 63), ALIAS),                     # y overlaps b's tail
+    (dict(y=P, ldy=128), ALIAS),                                 # same start, other stride
+    (dict(layout=GU, b=None, lda=128, y=P + 2 * 64 - 2, ldy=128), ALIAS),  # off by one element
+    (dict(layout=GU, b=None, lda=128, y=P + 2 * 64, ldy=256, rows=2), ALIAS),
+])
+def test_fwd_rejects(args, want):
+    assert fwd(**args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(kind=7), ENUM), (dict(inplace=3), INPLACE), (dict(rows=-2), SHAPE),
+    (dict(rows=0, a=None, b=None, dy=None, da=None, db=None), OK),
+    (dict(dy=None), NULL), (dict(da=None), NULL), (dict(db=None), NULL), (dict(a=None), NULL),
+    (dict(lddy=1), STRIDE), (dict(ldda=3), STRIDE), (dict(lddb=63), STRIDE),
+    (dict(inplace=1), INPLACE), (dict(inplace=1, da=None), INPLACE), (dict(inplace=1, db=None), INPLACE),
+    (dict(db=P + (3 << 20)), ALIAS),                              # da == db exactly: two writers
+    (dict(db=P + (3 << 20) + 2), ALIAS),                          # da, db overlap
+    (dict(da=P + 2), ALIAS),                                      # da straddles a
+    (dict(db=P + (2 << 20) + 64), ALIAS),                         # db overlaps dy partially
+    (dict(layout=GU, b=None, lda=128, ldda=128), NULL),           # gate_up dx: db must be NULL
+    (dict(layout=GU, b=None, lda=128, db=None, ldda=127), STRIDE),
+    (dict(layout=GU, b=None, lda=128, db=None, da=P + 2, ldda=128), ALIAS),
+    (dict(inplace=1, da=None, db=None, dy=P + 2), ALIAS),         # dy overlaps a, not exactly
+])
+def test_bwd_rejects(args, want):
+    assert bwd(**args) == want
+
+
+def _compile_host(src: str, tmp: str) -> str:
+    exe = os.path.join(tmp, "t")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-D__HIP_PLATFORM_AMD__", f"-I{CSRC}",
+                    "-I/opt/rocm/include", "-x", "c++", "-", "-o", exe], input=src, text=True, check=True)
+    return exe
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_row_divider_is_exact():
+    """The kernels divide unit indices by units-per-row with a multiply-high;
+    check the host-computed constants against plain division for every
+    divisor shape that matters and numerators up to 2^31."""
+    src = r'''
+#include "glu_internal.h"
+#include <cstdio>
+#include <random>
+int main() {
+  std::mt19937_64 rng(1);
+  const uint32_t ds[] = {1, 2, 3, 5, 7, 8, 9, 128, 1376, 1792, 2368, 1000003, 65535, 65536, 65537,
+                         (1u << 30) - 1, 1u << 30, 2147483647u};
+  long bad = 0;
+  for (uint32_t d : ds) {
+    glu::Divider v = glu::make_divider(d);
+    auto q = [&](uint32_t n) { return (uint32_t)((((uint64_t)n * v.magic) >> 32) + n) >> v.shift; };
+    for (uint32_t n = 0; n < 200000; ++n) bad += q(n) != n / d;
+    for (int i = 0; i < 2000000; ++i) { uint32_t n = rng() & 0x7fffffffu; bad += q(n) != n / d; }
+    for (uint32_t k = 0; k < 4096; ++k) { uint64_t n = (uint64_t)d * k; if (n < (1ull << 31)) {
+      bad += q((uint32_t)n) != k; if (n) bad += q((uint32_t)n - 1) != k - 1; } }
+    bad += q(0x7fffffffu) != 0x7fffffffu / d;
+  }
+  printf("%ld\n", bad);
+  return 0;
+}'''
+    with tempfile.TemporaryDirectory() as tmp:
+        out = subprocess.run([_compile_host(src, tmp)], capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "0"
+
+
+@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="needs hipcc")
+def test_kernel_isa():
+    """The compiled gfx950 kernels: no MFMA and no packed fp32 ops anywhere,
+    no fp64 in the bf16/fp16 kernels, and every vector kernel moves each of
+    its streams with 16-byte loads/stores (GLU_UNROLL per thread)."""
+    from mlp_gated_activation_amd import build as b
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [b.HIPCC, *[f for f in b.FLAGS if f not in ("-shared",)], f"-I{b.INCLUDE}", f"-I{b.CSRC}",
+               "--save-temps", "-c", b.SOURCES[0], "-o", os.path.join(tmp, "k.o")]
+        subprocess.run(cmd, cwd=tmp, check=True, capture_output=True)
+        asm = open(os.path.join(tmp, "glu_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")).read()
+    unroll = int(re.search(r"#define GLU_UNROLL (\d+)", open(os.path.join(CSRC, "glu_internal.h")).read()).group(1))
+    starts = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\w*glu_kernel\w*):", asm, re.M)]
+    assert len(starts) == 48
+    for pos, name in starts:
+        body = asm[pos:asm.find("s_endpgm", pos)]
+        assert "mfma" not in body, name
+        assert not re.search(r"v_pk_(add|mul|fma)_f32", body), name
+        m = re.search(r"glu_kernelINS0_(\w+?)ELi(\d)ELb(\d)ELb(\d)E", name)
+        storage, bwd, vec = m.group(1), m.group(3) == "1", m.group(4) == "1"
+        if storage != "4SF32":
+            assert not re.search(r"^\s+v_\w+_f64", body, re.M), name
+        if vec:
+            assert len(re.findall("global_load_dwordx4", body)) == unroll * (3 if bwd else 2), name
+            assert len(re.findall("global_store_dwordx4", body)) == unroll * (2 if bwd else 1), name
