@@ -38,7 +38,8 @@ BWD_BYTES = 5 * N * ES          # read a, b, dy; write da, db
 STEP_BYTES = FWD_BYTES + BWD_BYTES
 KERNEL_SOURCES = ["mlp_gated_activation_amd/csrc/glu_kernels.hip",
                   "mlp_gated_activation_amd/csrc/glu_internal.h",
-                  "mlp_gated_activation_amd/csrc/glu_taylor.h"]
+                  "mlp_gated_activation_amd/csrc/glu_taylor.h",
+                  "mlp_gated_activation_amd/csrc/glu_erfc.h"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_glu_swiglu_bf16_4096x14336.md")
 
 
@@ -69,11 +70,11 @@ def committed_traffic():
 def cpu_baseline(a, b, dy):
     """The fp64 oracle, as it stands, on the same inputs: fwd then bwd over
     the whole (4096, 14336) batch, repeated while under ~10 s; best time."""
-    import numpy as np
+    import torch
     import oracle
-    fa = a.to(dtype=__import__("torch").float64).numpy()
-    fb = b.to(dtype=__import__("torch").float64).numpy()
-    fdy = dy.to(dtype=__import__("torch").float64).numpy()
+    fa = a.to(torch.float64).numpy()
+    fb = b.to(torch.float64).numpy()
+    fdy = dy.to(torch.float64).numpy()
     oracle.fwd("silu", fa[:8], fb[:8])          # load/compile outside the timing
     times = []
     t_all = time.perf_counter()
@@ -100,11 +101,12 @@ def cpu_baseline(a, b, dy):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets (470 MB each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-check", action="store_true", default=True)
+    ap.add_argument("--no-copy-check", dest="copy_check", action="store_false",
+                    help="skip the torch device-copy reference")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -141,30 +143,38 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    def timed(fn, n):
+        """n launches of fn(i) bracketed by HIP events on the launch stream."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    # Headline: K whole steps, nothing between the launches.
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        a, b, dy, y = sets[i % len(sets)]
-        e0, e1, e2 = ev[i]
-        e0.record(stream)
-        glu.glu_fwd("silu", "separate", a, b, y)
-        e1.record(stream)
-        glu.glu_bwd("silu", "separate", a, b, dy, inplace=True)
-        e2.record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    total_ms = timed(step, args.steps)
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
-    mean = lambda v: sum(v) / len(v)
-    med = lambda v: v[len(v) // 2]
     ms_per_step = total_ms / args.steps
     value = STEP_BYTES / (ms_per_step * 1e-3) / 1e9
+
+    # Per-kernel average launch durations: K launches of each kernel alone
+    # (rotating buffer sets, so every launch streams cold memory).
+    def fwd_only(i):
+        a, b, dy, y = sets[i % len(sets)]
+        glu.glu_fwd("silu", "separate", a, b, y)
+
+    def bwd_only(i):
+        a, b, dy, y = sets[i % len(sets)]
+        glu.glu_bwd("silu", "separate", a, b, dy, inplace=True)
+
+    fwd_avg = timed(fwd_only, args.steps) / args.steps
+    bwd_avg = timed(bwd_only, args.steps) / args.steps
 
     # attainable reference: a plain device copy (1 read + 1 write) of the same bytes
     copy = None
@@ -186,7 +196,6 @@ def main():
         copy = round(copy_gbs, 1)
         del src, dsts
 
-    bwd_avg = mean(bwd_ms)
     achieved = BWD_BYTES / (bwd_avg * 1e-3) / 1e9
     traffic = committed_traffic()
     result = {
@@ -210,13 +219,11 @@ def main():
         },
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "kernels": {
-            "fwd": {"avg_us": round(1e3 * mean(fwd_ms), 2), "median_us": round(1e3 * med(fwd_ms), 2),
-                    "GBps": round(FWD_BYTES / (mean(fwd_ms) * 1e-3) / 1e9, 1), "bytes": FWD_BYTES},
-            "bwd": {"avg_us": round(1e3 * bwd_avg, 2), "median_us": round(1e3 * med(bwd_ms), 2),
-                    "GBps": round(achieved, 1), "bytes": BWD_BYTES},
+            "fwd": {"avg_us": round(1e3 * fwd_avg, 2), "GBps": round(FWD_BYTES / (fwd_avg * 1e-3) / 1e9, 1),
+                    "bytes": FWD_BYTES},
+            "bwd": {"avg_us": round(1e3 * bwd_avg, 2), "GBps": round(achieved, 1), "bytes": BWD_BYTES},
         },
-        "copy_GBps": copy,
-        "pct_of_copy": round(100 * value / copy, 2) if copy else None,
+        "torch_copy_GBps": copy,
         "wall_s_timed": round(wall, 4),
         "roofline": {
             "bound": "hbm",

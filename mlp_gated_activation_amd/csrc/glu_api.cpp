@@ -123,9 +123,12 @@ glu_status enqueue(int dtype, int kind, bool bwd, int64_t rows, int64_t cols, Ar
         return glu::launch(dtype, kind, bwd, vec, p, stream) == hipSuccess ? GLU_OK : GLU_ERR_HIP;
     };
 
+    // Each launch covers at most kMaxUnitsPerLaunch units and rows of at most
+    // max_cols elements (32-bit column indices in the kernel).
     const int64_t maxu = glu::kMaxUnitsPerLaunch;
-    if (upr <= maxu) {
-        const int64_t rows_per = maxu / upr;
+    const int64_t max_cols = glu::kMaxColsPerLaunch < maxu * ve ? glu::kMaxColsPerLaunch : maxu * ve;
+    if (cols <= max_cols) {
+        const int64_t rows_per = maxu / upr;   // >= 1 since upr <= max_cols / ve <= maxu
         for (int64_t r0 = 0; r0 < rows; r0 += rows_per) {
             int64_t n = rows - r0 < rows_per ? rows - r0 : rows_per;
             glu_status s = run(r0, n, 0, cols);
@@ -133,11 +136,10 @@ glu_status enqueue(int dtype, int kind, bool bwd, int64_t rows, int64_t cols, Ar
                 return s;
         }
     } else {
-        // a single row longer than one launch: split it into column chunks
-        const int64_t chunk = maxu * ve;
+        // rows longer than one launch: split each into column chunks
         for (int64_t r0 = 0; r0 < rows; ++r0)
-            for (int64_t c0 = 0; c0 < cols; c0 += chunk) {
-                glu_status s = run(r0, 1, c0, cols - c0 < chunk ? cols - c0 : chunk);
+            for (int64_t c0 = 0; c0 < cols; c0 += max_cols) {
+                glu_status s = run(r0, 1, c0, cols - c0 < max_cols ? cols - c0 : max_cols);
                 if (s != GLU_OK)
                     return s;
             }

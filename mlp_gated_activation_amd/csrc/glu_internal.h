@@ -10,17 +10,37 @@ namespace glu {
 // Launch shape.  A "unit" is one 16-byte vector of every stream (8 bf16/fp16
 // or 4 fp32 elements), or a single element on the unaligned path.  Each
 // thread owns GLU_UNROLL units, BLOCK apart, so every wave's accesses to a
-// stream are contiguous 1 KiB runs.
+// stream are contiguous 1 KiB runs.  The defaults come from a sweep on
+// MI355X (block 128..1024, unroll 1..8, with and without non-temporal
+// hints): many short-lived 512-thread blocks with one vector per stream per
+// thread moved the most bytes.
 #ifndef GLU_BLOCK
-#define GLU_BLOCK 256
+#define GLU_BLOCK 512
 #endif
 #ifndef GLU_UNROLL
-#define GLU_UNROLL 2
+#define GLU_UNROLL 1
+#endif
+// 1: 16-byte loads / stores carry the non-temporal hint (streamed, not kept).
+#ifndef GLU_NT
+#define GLU_NT 1
+#endif
+#ifndef GLU_NT_LOAD
+#define GLU_NT_LOAD GLU_NT
+#endif
+#ifndef GLU_NT_STORE
+#define GLU_NT_STORE GLU_NT
+#endif
+// 1: remap block ids so each of the 8 XCDs walks one contiguous slice.
+#ifndef GLU_XCD_REMAP
+#define GLU_XCD_REMAP 0
 #endif
 
 // Largest unit count one launch covers; keeps every per-launch index below
 // 2^31, which the kernels' 32-bit unsigned division relies on.
 constexpr uint32_t kMaxUnitsPerLaunch = 1u << 30;
+// Widest row (in elements) one launch covers: column indices stay 32-bit
+// with room for one more vector.  Longer rows are split into column chunks.
+constexpr int64_t kMaxColsPerLaunch = int64_t(1) << 31;
 
 // Division by a runtime constant d >= 1 for numerators n < 2^31:
 //   n / d == (umulhi(n, magic) + n) >> shift

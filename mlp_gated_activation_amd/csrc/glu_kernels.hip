@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "glu_erfc.h"
 #include "glu_internal.h"
 #include "glu_taylor.h"
 
@@ -141,8 +142,13 @@ __device__ inline double fabs_(double x) { return __builtin_fabs(x); }
 __device__ inline float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
 __device__ inline double fma_(double a, double b, double c) { return __builtin_fma(a, b, c); }
 
+// exp for the fp32 math of bf16/fp16 data: 2^(x log2 e) on the hardware
+// exponential (exp2f keeps subnormal results).  Rounding x*log2(e) to fp32
+// costs a relative error of about |x| * 6e-8 (under 4e-6 wherever a bf16 or
+// fp16 result is not zero), far inside half an output ulp (2^-9 / 2^-12).
+// The fp64 math of fp32 data uses the library exp.
 template <typename M> __device__ inline M ex(M x);
-template <> __device__ inline float ex<float>(float x) { return expf(x); }
+template <> __device__ inline float ex<float>(float x) { return exp2f(x * 1.44269504088896341f); }
 template <> __device__ inline double ex<double>(double x) { return exp(x); }
 template <typename M> __device__ inline M erfc_(M x);
 template <> __device__ inline float erfc_<float>(float x) { return erfcf(x); }
@@ -152,6 +158,23 @@ constexpr double kInvSqrt2 = 0.70710678118654752440;      // [SWIGLU] reasoning 
 constexpr double kInvSqrt2Pi = 0.39894228040143267794;
 constexpr double kSqrt2OverPi = 0.79788456080286535588;   // [SWIGLU] failure modes
 constexpr double kTanhCubic = 0.044715;
+
+// Normal CDF Phi(x) and E = exp(-x^2/2) in fp32, branch-free (see gen_erfc.py):
+//   t = 1/(1 + |x|/(2 sqrt 2)),  h = Phi(-|x|) = 0.5 t Q(t) E,  Phi = x >= 0 ? 1 - h : h.
+// One exp serves Phi and the density phi = E/sqrt(2 pi).  Relative error of
+// Phi about 6e-7 over all fp16/bf16 inputs; no 1 + erf cancellation.
+__device__ inline void norm_cdf(float x, float &Phi, float &E)
+{
+    constexpr float c[GLU_ERFC_Q_DEG + 1] = GLU_ERFC_Q_COEFFS;
+    const float t = recip(1.0f + fabs_(x) * float(0.5 * kInvSqrt2));
+    float q = c[GLU_ERFC_Q_DEG];
+#pragma unroll
+    for (int k = GLU_ERFC_Q_DEG - 1; k >= 0; --k)
+        q = fma_(q, t, c[k]);
+    E = ex<float>(-0.5f * x * x);
+    const float h = (0.5f * t * q) * E;
+    Phi = x >= 0.0f ? 1.0f - h : h;
+}
 
 // Clamp for the tanh form's polynomial: beyond |x| = 16 its sigmoid is 0 or
 // 1 in fp32 (and its contribution below any fp32/bf16/fp16 subnormal), while
@@ -167,17 +190,23 @@ template <int KIND, typename M> __device__ inline M act(M x)
         // silu(x) = x * sigmoid(x): [SWIGLU] reasoning step 5; [LIGER] Forward Pass
         M e = ex<M>(-fabs_(x));
         M q = recip(M(1) + e);
-        return x * (x >= M(0) ? q : e * q);
+        return x * (q * (x >= M(0) ? M(1) : e));
     } else if constexpr (KIND == GELU_ERF) {
-        // x * Phi(x), Phi(x) = erfc(-x/sqrt2)/2 (no 1+erf cancellation): reasoning step 7
-        return x * (M(0.5) * erfc_<M>(x * M(-kInvSqrt2)));
+        // x * Phi(x), Phi(x) = (1 + erf(x/sqrt2))/2 = erfc(-x/sqrt2)/2: reasoning step 7
+        if constexpr (sizeof(M) == 4) {
+            float Phi, E;
+            norm_cdf(x, Phi, E);
+            return x * Phi;
+        } else {
+            return x * (M(0.5) * erfc_<M>(x * M(-kInvSqrt2)));
+        }
     } else if constexpr (KIND == GELU_TANH) {
         // 0.5*x*(1+tanh(u)) = x * sigmoid(2u), u = sqrt(2/pi)(x + 0.044715 x^3)
         M xc = tanh_clamp(x);
         M w = xc * fma_(M(2 * kSqrt2OverPi * kTanhCubic), xc * xc, M(2 * kSqrt2OverPi));
         M e = ex<M>(-fabs_(w));
         M q = recip(M(1) + e);
-        return x * (w >= M(0) ? q : e * q);
+        return x * (q * (w >= M(0) ? M(1) : e));
     } else {
         // relu, NaN-propagating: [SWIGLU] Purpose (ReGLU)
         return x > M(0) ? x : (x != x ? x : M(0));
@@ -218,33 +247,45 @@ template <int KIND, bool PATCH, typename M> __device__ inline void act_grad(M x,
         // silu' = s*(1 + x*(1-s)): [SWIGLU] correctness requirements; [LIGER]
         // Backward Pass.  With e = exp(-|x|), q = 1/(1+e):
         //   x >= 0:  q^2 * ((1+e) + x*e)
-        //   x <  0:  e*q^2 * ((1+x) + e)   (the root's cancellation is this one sum)
+        //   x <  0:  e*q^2 * ((1+e) + x)     (the root's cancellation is this one sum)
+        // i.e. g = q^2 * s * fma(x, m, 1+e) with (s, m) = (1, e) or (e, 1):
+        // selects only, no divergent branch.
         M e = ex<M>(-fabs_(x));
         M q = recip(M(1) + e);
-        M q2 = q * q;
         bool pos = x >= M(0);
-        f = x * (pos ? q : e * q);
-        g = pos ? q2 * fma_(x, e, M(1) + e) : (e * q2) * ((M(1) + x) + e);
+        M sg = pos ? M(1) : e;
+        M m = pos ? e : M(1);
+        f = x * (q * sg);
+        g = (q * q) * sg * fma_(x, m, M(1) + e);
     } else if constexpr (KIND == GELU_ERF) {
         // d/dx [x Phi(x)] = Phi(x) + x phi(x)
-        M Phi = M(0.5) * erfc_<M>(x * M(-kInvSqrt2));
-        M phi = ex<M>(M(-0.5) * x * x) * M(kInvSqrt2Pi);
+        M Phi, phi;
+        if constexpr (sizeof(M) == 4) {
+            float E;
+            norm_cdf(x, Phi, E);
+            phi = E * float(kInvSqrt2Pi);
+        } else {
+            Phi = M(0.5) * erfc_<M>(x * M(-kInvSqrt2));
+            phi = ex<M>(M(-0.5) * x * x) * M(kInvSqrt2Pi);
+        }
         f = x * Phi;
         g = fma_(x, phi, Phi);
     } else if constexpr (KIND == GELU_TANH) {
         // w = 2u, v = 2x u'; sigmoid(w) (1 + v sigmoid(-w)):
         //   w >= 0:  q^2 * ((1+e) + v*e)
         //   w <  0:  e*q^2 * ((1+e) + v)
+        // folded into selects as for silu'.
         M xc = tanh_clamp(x);
         M x2 = xc * xc;
         M w = xc * fma_(M(2 * kSqrt2OverPi * kTanhCubic), x2, M(2 * kSqrt2OverPi));
         M v = xc * fma_(M(6 * kSqrt2OverPi * kTanhCubic), x2, M(2 * kSqrt2OverPi));
         M e = ex<M>(-fabs_(w));
         M q = recip(M(1) + e);
-        M q2 = q * q;
         bool pos = w >= M(0);
-        f = x * (pos ? q : e * q);
-        g = pos ? q2 * fma_(v, e, M(1) + e) : (e * q2) * ((M(1) + e) + v);
+        M sg = pos ? M(1) : e;
+        M m = pos ? e : M(1);
+        f = x * (q * sg);
+        g = (q * q) * sg * fma_(v, m, M(1) + e);
         if (x != x)
             g = x;
     } else {
@@ -265,14 +306,23 @@ template <int KIND, bool PATCH, typename M> __device__ inline void act_grad(M x,
 template <typename T>
 __device__ inline u32x4 ldv(const void *base, int64_t off_elems)
 {
-    return __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4 *>(static_cast<const char *>(base) + off_elems * T::SIZE));
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const char *>(base) + off_elems * T::SIZE);
+#if GLU_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
 }
 
 template <typename T>
 __device__ inline void stv(void *base, int64_t off_elems, u32x4 v)
 {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(static_cast<char *>(base) + off_elems * T::SIZE));
+    u32x4 *p = reinterpret_cast<u32x4 *>(static_cast<char *>(base) + off_elems * T::SIZE);
+#if GLU_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
 }
 
 __device__ inline const void *at(const void *base, int64_t off, int size)
@@ -281,14 +331,23 @@ __device__ inline const void *at(const void *base, int64_t off, int size)
 }
 __device__ inline void *at(void *base, int64_t off, int size) { return static_cast<char *>(base) + off * size; }
 
-template <typename T, int KIND, bool BWD, bool VEC>
+template <typename T, int KIND, bool BWD, bool VEC, bool FLAT>
 __global__ void __launch_bounds__(GLU_BLOCK) glu_kernel(const Args p)
 {
     using M = typename T::M;
     constexpr int VE = VEC ? T::VE : 1;
     constexpr int U = GLU_UNROLL;
 
+#if GLU_XCD_REMAP
+    // Blocks are dispatched round-robin over the 8 XCDs; give XCD x the
+    // x-th contiguous eighth of the blocks (when the grid divides evenly).
+    uint32_t bid = blockIdx.x;
+    if ((gridDim.x & 7u) == 0)
+        bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
+    const uint32_t first = bid * uint32_t(GLU_BLOCK * U) + threadIdx.x;
+#else
     const uint32_t first = blockIdx.x * uint32_t(GLU_BLOCK * U) + threadIdx.x;
+#endif
 
     uint32_t row[U], col[U];
     bool live[U], full[U];
@@ -299,7 +358,8 @@ __global__ void __launch_bounds__(GLU_BLOCK) glu_kernel(const Args p)
     for (int k = 0; k < U; ++k) {
         uint32_t u = first + uint32_t(k * GLU_BLOCK);
         live[k] = u < p.units;
-        uint32_t r = (__umulhi(u, p.row_div.magic) + u) >> p.row_div.shift;
+        // FLAT: the launch is a single row (dense operands merged), no division
+        uint32_t r = FLAT ? 0u : (__umulhi(u, p.row_div.magic) + u) >> p.row_div.shift;
         row[k] = r;
         col[k] = (u - r * p.units_per_row) * uint32_t(VE);
         full[k] = live[k] && (col[k] + uint32_t(VE) <= p.cols);
@@ -368,19 +428,20 @@ __global__ void __launch_bounds__(GLU_BLOCK) glu_kernel(const Args p)
 typedef void (*KernelFn)(const Args);
 
 template <typename T, int KIND, bool BWD>
-constexpr KernelFn pick(bool vec)
+constexpr KernelFn pick(bool vec, bool flat)
 {
-    return vec ? &glu_kernel<T, KIND, BWD, true> : &glu_kernel<T, KIND, BWD, false>;
+    return vec ? (flat ? &glu_kernel<T, KIND, BWD, true, true> : &glu_kernel<T, KIND, BWD, true, false>)
+               : (flat ? &glu_kernel<T, KIND, BWD, false, true> : &glu_kernel<T, KIND, BWD, false, false>);
 }
 
 template <typename T>
-KernelFn pick_kind(int kind, bool bwd, bool vec)
+KernelFn pick_kind(int kind, bool bwd, bool vec, bool flat)
 {
     switch (kind) {
-    case SILU: return bwd ? pick<T, SILU, true>(vec) : pick<T, SILU, false>(vec);
-    case GELU_ERF: return bwd ? pick<T, GELU_ERF, true>(vec) : pick<T, GELU_ERF, false>(vec);
-    case GELU_TANH: return bwd ? pick<T, GELU_TANH, true>(vec) : pick<T, GELU_TANH, false>(vec);
-    default: return bwd ? pick<T, RELU, true>(vec) : pick<T, RELU, false>(vec);
+    case SILU: return bwd ? pick<T, SILU, true>(vec, flat) : pick<T, SILU, false>(vec, flat);
+    case GELU_ERF: return bwd ? pick<T, GELU_ERF, true>(vec, flat) : pick<T, GELU_ERF, false>(vec, flat);
+    case GELU_TANH: return bwd ? pick<T, GELU_TANH, true>(vec, flat) : pick<T, GELU_TANH, false>(vec, flat);
+    default: return bwd ? pick<T, RELU, true>(vec, flat) : pick<T, RELU, false>(vec, flat);
     }
 }
 
@@ -388,9 +449,11 @@ KernelFn pick_kind(int kind, bool bwd, bool vec)
 
 hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args, hipStream_t stream)
 {
-    KernelFn fn = dtype == F32 ? pick_kind<SF32>(kind, backward, vec)
-                : dtype == F16 ? pick_kind<SF16>(kind, backward, vec)
-                               : pick_kind<SBf16>(kind, backward, vec);
+    // a launch whose units all lie in one row needs no row division
+    const bool flat = args.units == args.units_per_row;
+    KernelFn fn = dtype == F32 ? pick_kind<SF32>(kind, backward, vec, flat)
+                : dtype == F16 ? pick_kind<SF16>(kind, backward, vec, flat)
+                               : pick_kind<SBf16>(kind, backward, vec, flat);
     const uint32_t per_block = uint32_t(GLU_BLOCK) * GLU_UNROLL;
     dim3 grid((args.units + per_block - 1) / per_block);
     dim3 block(GLU_BLOCK);

