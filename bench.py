@@ -227,7 +227,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "glu_kernel<bf16, silu, bwd, vec>",
+            "kernel": "glu_kernel<bf16, silu, bwd, vec, flat>",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -12,10 +12,10 @@ namespace glu {
 // thread owns GLU_UNROLL units, BLOCK apart, so every wave's accesses to a
 // stream are contiguous 1 KiB runs.  The defaults come from a sweep on
 // MI355X (block 128..1024, unroll 1..8, with and without non-temporal
-// hints): many short-lived 512-thread blocks with one vector per stream per
+// hints): many short-lived 128-thread blocks with one vector per stream per
 // thread moved the most bytes.
 #ifndef GLU_BLOCK
-#define GLU_BLOCK 512
+#define GLU_BLOCK 128
 #endif
 #ifndef GLU_UNROLL
 #define GLU_UNROLL 1
