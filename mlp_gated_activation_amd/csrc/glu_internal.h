@@ -10,12 +10,19 @@ namespace glu {
 // Launch shape.  A "unit" is one 16-byte vector of every stream (8 bf16/fp16
 // or 4 fp32 elements), or a single element on the unaligned path.  Each
 // thread owns GLU_UNROLL units, BLOCK apart, so every wave's accesses to a
-// stream are contiguous 1 KiB runs.  The defaults come from a sweep on
-// MI355X (block 128..1024, unroll 1..8, with and without non-temporal
-// hints): many short-lived 128-thread blocks with one vector per stream per
-// thread moved the most bytes.
+// stream are contiguous 1 KiB runs.  The defaults come from sweeps on
+// MI355X (block 64..1024, unroll 1..8, with and without non-temporal hints,
+// median of 3-5 interleaved rounds): many short-lived blocks with one vector
+// per stream per thread moved the most bytes -- 64 threads for the forward
+// (3 streams), 128 for the backward (5 streams).
 #ifndef GLU_BLOCK
 #define GLU_BLOCK 128
+#endif
+#ifndef GLU_BLOCK_FWD
+#define GLU_BLOCK_FWD 64
+#endif
+#ifndef GLU_BLOCK_BWD
+#define GLU_BLOCK_BWD GLU_BLOCK
 #endif
 #ifndef GLU_UNROLL
 #define GLU_UNROLL 1
@@ -29,6 +36,11 @@ namespace glu {
 #endif
 #ifndef GLU_NT_STORE
 #define GLU_NT_STORE GLU_NT
+#endif
+// 1: sigmoids of bf16/fp16 data use the raw hardware exp on a 2^16-scaled
+// argument (2 instructions) instead of the subnormal-safe exp2f (7).
+#ifndef GLU_SCALED_EXP
+#define GLU_SCALED_EXP 1
 #endif
 // 1: remap block ids so each of the 8 XCDs walks one contiguous slice.
 #ifndef GLU_XCD_REMAP

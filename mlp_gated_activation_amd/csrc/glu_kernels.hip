@@ -147,6 +147,34 @@ __device__ inline double fma_(double a, double b, double c) { return __builtin_f
 // costs a relative error of about |x| * 6e-8 (under 4e-6 wherever a bf16 or
 // fp16 result is not zero), far inside half an output ulp (2^-9 / 2^-12).
 // The fp64 math of fp32 data uses the library exp.
+// Sigmoid pieces from a = |x| (or |w|) >= 0:  e = exp(-a), q = 1/(1 + e).
+// fp32 (bf16/fp16 data): es = e * 2^16 = 2^(16 - a log2(e)) from the raw
+// hardware exponential; es is normal for a < 98.4, and beyond that every
+// product with e is below half the smallest bf16/fp16 subnormal, so the
+// hardware's flush to zero there is harmless.  Rounding the argument near 16
+// costs at most 6.6e-7 relative in e.  fp64 (fp32 data): library exp.
+struct SigParts {
+    float e, q;
+};
+__device__ inline SigParts sig_parts(float a)
+{
+#if GLU_SCALED_EXP
+    const float es = __builtin_amdgcn_exp2f(__builtin_fmaf(a, -1.44269504088896341f, 16.0f));
+    return SigParts{es * 0x1p-16f, __builtin_amdgcn_rcpf(__builtin_fmaf(es, 0x1p-16f, 1.0f))};
+#else
+    const float e = exp2f(a * -1.44269504088896341f);
+    return SigParts{e, __builtin_amdgcn_rcpf(1.0f + e)};
+#endif
+}
+struct SigPartsD {
+    double e, q;
+};
+__device__ inline SigPartsD sig_parts(double a)
+{
+    const double e = exp(-a);
+    return SigPartsD{e, 1.0 / (1.0 + e)};
+}
+
 template <typename M> __device__ inline M ex(M x);
 template <> __device__ inline float ex<float>(float x) { return exp2f(x * 1.44269504088896341f); }
 template <> __device__ inline double ex<double>(double x) { return exp(x); }
@@ -159,11 +187,16 @@ constexpr double kInvSqrt2Pi = 0.39894228040143267794;
 constexpr double kSqrt2OverPi = 0.79788456080286535588;   // [SWIGLU] failure modes
 constexpr double kTanhCubic = 0.044715;
 
-// Normal CDF Phi(x) and E = exp(-x^2/2) in fp32, branch-free (see gen_erfc.py):
-//   t = 1/(1 + |x|/(2 sqrt 2)),  h = Phi(-|x|) = 0.5 t Q(t) E,  Phi = x >= 0 ? 1 - h : h.
-// One exp serves Phi and the density phi = E/sqrt(2 pi).  Relative error of
-// Phi about 6e-7 over all fp16/bf16 inputs; no 1 + erf cancellation.
-__device__ inline void norm_cdf(float x, float &Phi, float &E)
+// Normal CDF Phi(x) and the density phi(x) in fp32, branch-free (see gen_erfc.py):
+//   t = 1/(1 + |x|/(2 sqrt 2)),  h = Phi(-|x|) = 0.5 t Q(t) E,  E = exp(-x^2/2),
+//   Phi = x >= 0 ? 1 - h : h,    phi = E / sqrt(2 pi).
+// E is taken from the hardware exponential as Es = E * 2^16 = 2^(16 - x^2 log2(e)/2),
+// which stays normal for |x| < 14 (beyond that Phi(-|x|) and phi are below
+// every bf16/fp16 subnormal); the 2^-16 goes into the final products, which
+// round subnormal results correctly.  One exp serves Phi and phi; relative
+// error of Phi about 1e-6 over all fp16/bf16 inputs; no 1 + erf cancellation.
+constexpr float kLog2e = 1.44269504088896341f;
+__device__ inline void norm_cdf(float x, float &Phi, float &phi)
 {
     constexpr float c[GLU_ERFC_Q_DEG + 1] = GLU_ERFC_Q_COEFFS;
     const float t = recip(1.0f + fabs_(x) * float(0.5 * kInvSqrt2));
@@ -171,9 +204,10 @@ __device__ inline void norm_cdf(float x, float &Phi, float &E)
 #pragma unroll
     for (int k = GLU_ERFC_Q_DEG - 1; k >= 0; --k)
         q = fma_(q, t, c[k]);
-    E = ex<float>(-0.5f * x * x);
-    const float h = (0.5f * t * q) * E;
+    const float Es = __builtin_amdgcn_exp2f(fma_(x * x, -0.5f * kLog2e, 16.0f));
+    const float h = (t * q * 0x1p-17f) * Es;
     Phi = x >= 0.0f ? 1.0f - h : h;
+    phi = Es * float(kInvSqrt2Pi * 0x1p-16);
 }
 
 // Clamp for the tanh form's polynomial: beyond |x| = 16 its sigmoid is 0 or
@@ -188,14 +222,13 @@ template <int KIND, typename M> __device__ inline M act(M x)
 {
     if constexpr (KIND == SILU) {
         // silu(x) = x * sigmoid(x): [SWIGLU] reasoning step 5; [LIGER] Forward Pass
-        M e = ex<M>(-fabs_(x));
-        M q = recip(M(1) + e);
-        return x * (q * (x >= M(0) ? M(1) : e));
+        const auto sp = sig_parts(fabs_(x));
+        return x * (sp.q * (x >= M(0) ? M(1) : sp.e));
     } else if constexpr (KIND == GELU_ERF) {
         // x * Phi(x), Phi(x) = (1 + erf(x/sqrt2))/2 = erfc(-x/sqrt2)/2: reasoning step 7
         if constexpr (sizeof(M) == 4) {
-            float Phi, E;
-            norm_cdf(x, Phi, E);
+            float Phi, phi;
+            norm_cdf(x, Phi, phi);
             return x * Phi;
         } else {
             return x * (M(0.5) * erfc_<M>(x * M(-kInvSqrt2)));
@@ -204,9 +237,8 @@ template <int KIND, typename M> __device__ inline M act(M x)
         // 0.5*x*(1+tanh(u)) = x * sigmoid(2u), u = sqrt(2/pi)(x + 0.044715 x^3)
         M xc = tanh_clamp(x);
         M w = xc * fma_(M(2 * kSqrt2OverPi * kTanhCubic), xc * xc, M(2 * kSqrt2OverPi));
-        M e = ex<M>(-fabs_(w));
-        M q = recip(M(1) + e);
-        return x * (q * (w >= M(0) ? M(1) : e));
+        const auto sp = sig_parts(fabs_(w));
+        return x * (sp.q * (w >= M(0) ? M(1) : sp.e));
     } else {
         // relu, NaN-propagating: [SWIGLU] Purpose (ReGLU)
         return x > M(0) ? x : (x != x ? x : M(0));
@@ -250,8 +282,8 @@ template <int KIND, bool PATCH, typename M> __device__ inline void act_grad(M x,
         //   x <  0:  e*q^2 * ((1+e) + x)     (the root's cancellation is this one sum)
         // i.e. g = q^2 * s * fma(x, m, 1+e) with (s, m) = (1, e) or (e, 1):
         // selects only, no divergent branch.
-        M e = ex<M>(-fabs_(x));
-        M q = recip(M(1) + e);
+        const auto sp = sig_parts(fabs_(x));
+        const M e = sp.e, q = sp.q;
         bool pos = x >= M(0);
         M sg = pos ? M(1) : e;
         M m = pos ? e : M(1);
@@ -261,9 +293,7 @@ template <int KIND, bool PATCH, typename M> __device__ inline void act_grad(M x,
         // d/dx [x Phi(x)] = Phi(x) + x phi(x)
         M Phi, phi;
         if constexpr (sizeof(M) == 4) {
-            float E;
-            norm_cdf(x, Phi, E);
-            phi = E * float(kInvSqrt2Pi);
+            norm_cdf(x, Phi, phi);
         } else {
             Phi = M(0.5) * erfc_<M>(x * M(-kInvSqrt2));
             phi = ex<M>(M(-0.5) * x * x) * M(kInvSqrt2Pi);
@@ -279,8 +309,8 @@ template <int KIND, bool PATCH, typename M> __device__ inline void act_grad(M x,
         M x2 = xc * xc;
         M w = xc * fma_(M(2 * kSqrt2OverPi * kTanhCubic), x2, M(2 * kSqrt2OverPi));
         M v = xc * fma_(M(6 * kSqrt2OverPi * kTanhCubic), x2, M(2 * kSqrt2OverPi));
-        M e = ex<M>(-fabs_(w));
-        M q = recip(M(1) + e);
+        const auto sp = sig_parts(fabs_(w));
+        const M e = sp.e, q = sp.q;
         bool pos = w >= M(0);
         M sg = pos ? M(1) : e;
         M m = pos ? e : M(1);
@@ -331,12 +361,15 @@ __device__ inline const void *at(const void *base, int64_t off, int size)
 }
 __device__ inline void *at(void *base, int64_t off, int size) { return static_cast<char *>(base) + off * size; }
 
+template <bool BWD> constexpr int block_size() { return BWD ? GLU_BLOCK_BWD : GLU_BLOCK_FWD; }
+
 template <typename T, int KIND, bool BWD, bool VEC, bool FLAT>
-__global__ void __launch_bounds__(GLU_BLOCK) glu_kernel(const Args p)
+__global__ void __launch_bounds__(block_size<BWD>()) glu_kernel(const Args p)
 {
     using M = typename T::M;
     constexpr int VE = VEC ? T::VE : 1;
     constexpr int U = GLU_UNROLL;
+    constexpr int BLOCK = block_size<BWD>();
 
 #if GLU_XCD_REMAP
     // Blocks are dispatched round-robin over the 8 XCDs; give XCD x the
@@ -344,9 +377,9 @@ __global__ void __launch_bounds__(GLU_BLOCK) glu_kernel(const Args p)
     uint32_t bid = blockIdx.x;
     if ((gridDim.x & 7u) == 0)
         bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
-    const uint32_t first = bid * uint32_t(GLU_BLOCK * U) + threadIdx.x;
+    const uint32_t first = bid * uint32_t(BLOCK * U) + threadIdx.x;
 #else
-    const uint32_t first = blockIdx.x * uint32_t(GLU_BLOCK * U) + threadIdx.x;
+    const uint32_t first = blockIdx.x * uint32_t(BLOCK * U) + threadIdx.x;
 #endif
 
     uint32_t row[U], col[U];
@@ -356,7 +389,7 @@ __global__ void __launch_bounds__(GLU_BLOCK) glu_kernel(const Args p)
     // Phase 1: locate every unit and issue all full-vector loads.
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-        uint32_t u = first + uint32_t(k * GLU_BLOCK);
+        uint32_t u = first + uint32_t(k * BLOCK);
         live[k] = u < p.units;
         // FLAT: the launch is a single row (dense operands merged), no division
         uint32_t r = FLAT ? 0u : (__umulhi(u, p.row_div.magic) + u) >> p.row_div.shift;
@@ -454,9 +487,10 @@ hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args
     KernelFn fn = dtype == F32 ? pick_kind<SF32>(kind, backward, vec, flat)
                 : dtype == F16 ? pick_kind<SF16>(kind, backward, vec, flat)
                                : pick_kind<SBf16>(kind, backward, vec, flat);
-    const uint32_t per_block = uint32_t(GLU_BLOCK) * GLU_UNROLL;
+    const uint32_t bs = backward ? GLU_BLOCK_BWD : GLU_BLOCK_FWD;
+    const uint32_t per_block = bs * GLU_UNROLL;
     dim3 grid((args.units + per_block - 1) / per_block);
-    dim3 block(GLU_BLOCK);
+    dim3 block(bs);
     Args copy = args;
     void *kargs[] = {&copy};
     return hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block, kargs, 0, stream);
