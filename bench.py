@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets (470 MB each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-torch-eager", dest="torch_eager", action="store_false",
+                    help="skip the torch eager comparison")
     ap.add_argument("--no-copy-check", dest="copy_check", action="store_false",
                     help="skip the torch device-copy reference")
     args = ap.parse_args()
@@ -176,6 +178,30 @@ def main():
     fwd_avg = timed(fwd_only, args.steps) / args.steps
     bwd_avg = timed(bwd_only, args.steps) / args.steps
 
+    # Context: the same step in plain torch eager (silu then multiply, and
+    # autograd for the gradients), timed the same way.
+    eager = None
+    if args.torch_eager:
+        import torch.nn.functional as F
+        reps = min(args.steps, 100)
+
+        def eager_fwd(i):
+            a, b, dy, y = sets[i % len(sets)]
+            F.silu(a) * b
+
+        def eager_step(i):
+            a, b, dy, y = sets[i % len(sets)]
+            a_ = a.detach().requires_grad_()
+            b_ = b.detach().requires_grad_()
+            (F.silu(a_) * b_).backward(dy)
+
+        t_ef = timed(eager_fwd, reps) / reps
+        t_es = timed(eager_step, reps) / reps
+        eager = {"fwd_us": round(1e3 * t_ef, 2), "fwd_GBps": round(FWD_BYTES / (t_ef * 1e-3) / 1e9, 1),
+                 "step_us": round(1e3 * t_es, 2), "step_GBps": round(STEP_BYTES / (t_es * 1e-3) / 1e9, 1),
+                 "speedup_step": round(t_es / ms_per_step, 2),
+                 "note": "F.silu(a) * b and autograd, bf16, same buffers; algorithmic bytes / time"}
+
     # attainable reference: a plain device copy (1 read + 1 write) of the same bytes
     copy = None
     if args.copy_check:
@@ -224,6 +250,7 @@ def main():
             "bwd": {"avg_us": round(1e3 * bwd_avg, 2), "GBps": round(achieved, 1), "bytes": BWD_BYTES},
         },
         "torch_copy_GBps": copy,
+        "torch_eager": eager,
         "wall_s_timed": round(wall, 4),
         "roofline": {
             "bound": "hbm",

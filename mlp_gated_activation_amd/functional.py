@@ -1,0 +1,143 @@
+"""Autograd functions and a gated-MLP module over the C ABI.
+
+"Kernel Profile: SwiGLU (Tier 1 -- Element-wise)":
+  * Identity: an autograd function (forward c = silu(a) * b), a functional
+    entry point and an MLP module;
+  * Backward Pass / Key Patterns: only a and b are saved, the sigmoid is
+    recomputed, and the gradients are written over the saved a and b;
+  * Module Parameters: gate, up and down projections without bias.
+"Write a Triton SiLU-Mul (SwiGLU) Kernel", Purpose: the MLP is
+down_proj(act(gate_proj(x)) * up_proj(x)), optionally with gate and up fused
+into one projection whose output is [gate | up] (Inputs, item 4).
+
+Every element of the activation and its gradient is computed by libglu.so;
+this module only wires it into autograd.  The projections are ordinary
+torch.nn.Linear layers (hipBLASLt GEMMs on ROCm).
+
+In-place backward (the default, as in the profile above): the gradient
+overwrites the saved activation inputs, which therefore must not be used by
+anything else after the backward.  Pass inplace_backward=False to keep them.
+"""
+from __future__ import annotations
+
+import torch
+import torch.nn as nn
+
+from . import glu as _glu
+
+_KINDS = ("silu", "gelu_erf", "gelu_tanh", "relu")
+
+
+def _ready(t: torch.Tensor) -> torch.Tensor:
+    """Incoming gradients may be views the ABI cannot take (broadcast rows
+    with stride 0, transposed or unmergeable views); make those contiguous
+    (this allocates)."""
+    if t.dim() == 0 or (t.shape[-1] > 1 and t.stride(-1) != 1):
+        return t.contiguous()
+    try:
+        v = t.view(-1, t.shape[-1])
+    except RuntimeError:
+        return t.contiguous()
+    if v.shape[0] > 1 and v.stride(0) < v.shape[1]:
+        return t.contiguous()
+    return t
+
+
+class GatedActivation(torch.autograd.Function):
+    """y = act(a) * b for separate a, b."""
+
+    @staticmethod
+    def forward(ctx, a, b, kind: str, inplace_backward: bool):
+        y = _glu.glu_fwd(kind, "separate", a, b)
+        ctx.save_for_backward(a, b)
+        ctx.kind = kind
+        ctx.inplace_backward = inplace_backward
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        a, b = ctx.saved_tensors
+        dy = _ready(dy)
+        if ctx.inplace_backward:
+            _glu.glu_bwd(ctx.kind, "separate", a, b, dy, inplace=True)
+            return a, b, None, None
+        da, db = _glu.glu_bwd(ctx.kind, "separate", a, b, dy, inplace=False)
+        return da, db, None, None
+
+
+class FusedGatedActivation(torch.autograd.Function):
+    """y = act(x[..., :I]) * x[..., I:] for the fused [gate | up] layout."""
+
+    @staticmethod
+    def forward(ctx, x, kind: str, inplace_backward: bool):
+        y = _glu.glu_fwd(kind, "gate_up", x)
+        ctx.save_for_backward(x)
+        ctx.kind = kind
+        ctx.inplace_backward = inplace_backward
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        (x,) = ctx.saved_tensors
+        dy = _ready(dy)
+        if ctx.inplace_backward:
+            _glu.glu_bwd(ctx.kind, "gate_up", x, None, dy, inplace=True)
+            return x, None, None
+        dx = _glu.glu_bwd(ctx.kind, "gate_up", x, None, dy, inplace=False)
+        return dx, None, None
+
+
+def gated_activation(a: torch.Tensor, b: torch.Tensor | None = None, kind: str = "silu",
+                     inplace_backward: bool = True) -> torch.Tensor:
+    """act(a) * b; with b None, a is the fused [gate | up] tensor."""
+    if kind not in _KINDS:
+        raise ValueError(f"unknown kind {kind!r}; expected one of {_KINDS}")
+    if b is None:
+        return FusedGatedActivation.apply(a, kind, inplace_backward)
+    return GatedActivation.apply(a, b, kind, inplace_backward)
+
+
+def swiglu(a, b=None, inplace_backward: bool = True):
+    """silu(a) * b (SwiGLU)."""
+    return gated_activation(a, b, "silu", inplace_backward)
+
+
+def geglu(a, b=None, approximate: str = "none", inplace_backward: bool = True):
+    """gelu(a) * b (GeGLU); approximate 'none' (erf form) or 'tanh'."""
+    if approximate not in ("none", "tanh"):
+        raise ValueError("approximate must be 'none' or 'tanh'")
+    return gated_activation(a, b, "gelu_erf" if approximate == "none" else "gelu_tanh", inplace_backward)
+
+
+def reglu(a, b=None, inplace_backward: bool = True):
+    """relu(a) * b (ReGLU)."""
+    return gated_activation(a, b, "relu", inplace_backward)
+
+
+class GatedMLP(nn.Module):
+    """down_proj(act(gate_proj(x)) * up_proj(x)) with the activation step on
+    the gfx950 kernels.  fused_gate_up=True keeps gate and up as one
+    projection of width 2*intermediate_size whose output is [gate | up]."""
+
+    def __init__(self, hidden_size: int, intermediate_size: int, kind: str = "silu",
+                 fused_gate_up: bool = True, inplace_backward: bool = True, device=None, dtype=None):
+        super().__init__()
+        if kind not in _KINDS:
+            raise ValueError(f"unknown kind {kind!r}")
+        self.kind = kind
+        self.fused_gate_up = fused_gate_up
+        self.inplace_backward = inplace_backward
+        kw = dict(bias=False, device=device, dtype=dtype)
+        if fused_gate_up:
+            self.gate_up_proj = nn.Linear(hidden_size, 2 * intermediate_size, **kw)
+        else:
+            self.gate_proj = nn.Linear(hidden_size, intermediate_size, **kw)
+            self.up_proj = nn.Linear(hidden_size, intermediate_size, **kw)
+        self.down_proj = nn.Linear(intermediate_size, hidden_size, **kw)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if self.fused_gate_up:
+            h = gated_activation(self.gate_up_proj(x), None, self.kind, self.inplace_backward)
+        else:
+            h = gated_activation(self.gate_proj(x), self.up_proj(x), self.kind, self.inplace_backward)
+        return self.down_proj(h)

@@ -1,0 +1,146 @@
+"""GPU tests of the autograd functions and the gated-MLP module.
+
+The activation and its gradient must match the fp64 oracle to one output
+ulp (they are the C-ABI kernels); the whole MLP must match a float64 CPU
+reference of the same network within bf16-GEMM error."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle.compare import compare
+
+pytestmark = pytest.mark.gpu
+FMT = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}
+KINDS = ("silu", "gelu_erf", "gelu_tanh", "relu")
+
+
+@pytest.fixture(scope="module")
+def fn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from conftest import ensure_built
+    ensure_built()
+    from mlp_gated_activation_amd import functional
+    return functional
+
+
+def f64(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def ok(got, ref, what):
+    rep = compare(f64(got), ref, FMT[got.dtype])
+    assert rep.ok, f"{what}: {rep}"
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("inplace", [True, False])
+def test_autograd_separate(fn, kind, inplace):
+    g = torch.Generator().manual_seed(31)
+    a0 = (torch.randn(300, 777, generator=g) * 2).to(torch.bfloat16).cuda().requires_grad_()
+    b0 = torch.randn(300, 777, generator=g).to(torch.bfloat16).cuda().requires_grad_()
+    dy = torch.randn(300, 777, generator=g).to(torch.bfloat16).cuda()
+    fa, fb, fdy = f64(a0), f64(b0), f64(dy)
+    # non-leaf inputs (as the outputs of the projections would be); x * 1 is exact
+    a, b = a0 * 1, b0 * 1
+    y = fn.gated_activation(a, b, kind, inplace_backward=inplace)
+    ok(y, oracle.fwd(kind, fa, fb), f"{kind} y")
+    y.backward(dy)
+    rda, rdb = oracle.bwd(kind, fa, fb, fdy)
+    ok(a0.grad, rda, f"{kind} da")
+    ok(b0.grad, rdb, f"{kind} db")
+    if not inplace:
+        assert torch.equal(a.detach(), a0.detach()), "out-of-place backward modified a"
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_autograd_fused(fn, kind):
+    g = torch.Generator().manual_seed(37)
+    x0 = (torch.randn(257, 2 * 1000, generator=g) * 1.5).to(torch.float16).cuda().requires_grad_()
+    dy = torch.randn(257, 1000, generator=g).to(torch.float16).cuda()
+    fx, fdy = f64(x0), f64(dy)
+    y = fn.gated_activation(x0 * 1, None, kind)
+    ok(y, oracle.fwd_gate_up(kind, fx), f"{kind} fused y")
+    y.backward(dy)
+    ok(x0.grad, oracle.bwd_gate_up(kind, fx, fdy), f"{kind} fused dx")
+
+
+def test_leaf_inputs_out_of_place(fn):
+    g = torch.Generator().manual_seed(41)
+    a = (torch.randn(64, 512, generator=g) * 2).to(torch.bfloat16).cuda().requires_grad_()
+    b = torch.randn(64, 512, generator=g).to(torch.bfloat16).cuda().requires_grad_()
+    keep_a, keep_b = a.detach().clone(), b.detach().clone()
+    y = fn.swiglu(a, b, inplace_backward=False)
+    y.sum().backward()
+    assert torch.equal(a.detach(), keep_a) and torch.equal(b.detach(), keep_b)
+    rda, rdb = oracle.bwd("silu", f64(keep_a), f64(keep_b), np.ones((64, 512)))
+    ok(a.grad, rda, "leaf da")
+    ok(b.grad, rdb, "leaf db")
+
+
+def test_expanded_incoming_gradient(fn):
+    """A broadcast (stride-0) incoming gradient is made contiguous first."""
+    g = torch.Generator().manual_seed(43)
+    a0 = (torch.randn(16, 256, generator=g) * 2).to(torch.bfloat16).cuda().requires_grad_()
+    b0 = torch.randn(16, 256, generator=g).to(torch.bfloat16).cuda().requires_grad_()
+    y = fn.geglu(a0 * 1, b0 * 1, approximate="tanh")
+    row = torch.randn(1, 256, generator=g).to(torch.bfloat16).cuda()
+    y.backward(row.expand(16, 256))
+    rda, rdb = oracle.bwd("gelu_tanh", f64(a0), f64(b0), np.broadcast_to(f64(row), (16, 256)))
+    ok(a0.grad, rda, "expanded dy da")
+    ok(b0.grad, rdb, "expanded dy db")
+
+
+def _reference_mlp(x, wgu, wd, kind, fused, inter):
+    """float64 CPU reference of the same network with torch's own activations."""
+    x = x.detach().cpu().double().requires_grad_()
+    wgu = [w.detach().cpu().double().requires_grad_() for w in wgu]
+    wd = wd.detach().cpu().double().requires_grad_()
+    if fused:
+        h = x @ wgu[0].t()
+        gate, up = h[:, :inter], h[:, inter:]
+    else:
+        gate, up = x @ wgu[0].t(), x @ wgu[1].t()
+    act = {"silu": F.silu, "relu": F.relu,
+           "gelu_erf": lambda v: F.gelu(v, approximate="none"),
+           "gelu_tanh": lambda v: F.gelu(v, approximate="tanh")}[kind]
+    out = (act(gate) * up) @ wd.t()
+    return x, wgu, wd, out
+
+
+def _rel(got, ref):
+    got = got.detach().cpu().double()
+    return float((got - ref).norm() / ref.norm())
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("fused", [True, False])
+def test_gated_mlp_matches_fp64_reference(fn, kind, fused):
+    torch.manual_seed(47)
+    hidden, inter, tokens = 256, 1000, 150
+    mlp = fn.GatedMLP(hidden, inter, kind=kind, fused_gate_up=fused, device="cuda", dtype=torch.bfloat16)
+    x = torch.randn(tokens, hidden, device="cuda", dtype=torch.bfloat16).requires_grad_()
+    out = mlp(x)
+    dout = torch.randn_like(out)
+    out.backward(dout)
+    wgu = [mlp.gate_up_proj.weight] if fused else [mlp.gate_proj.weight, mlp.up_proj.weight]
+    rx, rw, rd, rout = _reference_mlp(x, wgu, mlp.down_proj.weight, kind, fused, inter)
+    rout.backward(dout.detach().cpu().double())
+    # bf16 GEMM inputs/outputs: a few 2^-8 relative per element, far less in norm
+    tol = 2e-2
+    assert _rel(out, rout) < tol
+    assert _rel(x.grad, rx.grad) < tol
+    assert _rel(mlp.down_proj.weight.grad, rd.grad) < tol
+    for w, r in zip(wgu, rw):
+        assert _rel(w.grad, r.grad) < tol
+
+
+def test_module_rejects_unknown_kind(fn):
+    with pytest.raises(ValueError):
+        fn.GatedMLP(8, 8, kind="swish")
+    with pytest.raises(ValueError):
+        fn.geglu(torch.zeros(1, 8, device="cuda"), torch.zeros(1, 8, device="cuda"), approximate="fast")
