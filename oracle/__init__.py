@@ -15,6 +15,7 @@ applies the ``[gate | up]`` layout, which is pure slicing:
 * "Kernel Profile: SwiGLU (Tier 1 -- Element-wise)" -- "Key Patterns": the
   backward writes ``da, db`` over the saved ``a, b``; in the fused layout the
   gradient is therefore ``dx = [da | db]``.
+* "Write a Triton Fused Add+RMSNorm Kernel": ``add_rmsnorm`` below.
 
 All inputs are the exact values of the stored (already rounded) tensors,
 given as float64 arrays; all outputs are unrounded float64.
@@ -66,6 +67,8 @@ def _load():
         lib.oracle_fwd.restype = None
         lib.oracle_bwd.argtypes = [ctypes.c_int, i64, pd, pd, pd, pd, pd]
         lib.oracle_bwd.restype = None
+        lib.oracle_add_rmsnorm.argtypes = [i64, i64, pd, pd, pd, d, pd, pd, pd]
+        lib.oracle_add_rmsnorm.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -161,3 +164,23 @@ def bwd_gate_up(kind, x, dy) -> np.ndarray:
     a, b = split_gate_up(x)
     da, db = bwd(kind, a, b, dy)
     return np.concatenate([da, db], axis=1)
+
+
+def add_rmsnorm(x, res, gamma, eps: float):
+    """Fused residual add + RMSNorm forward over the last dimension.
+
+    x, res: (rows, H); gamma: (H,).  Returns (h, y, rstd): h = x + res,
+    rstd = 1/sqrt(mean(h^2) + eps) per row, y = h * rstd * gamma.
+    """
+    x = _f64(x)
+    res = _f64(res)
+    gamma = _f64(gamma)
+    if x.ndim != 2 or x.shape != res.shape or gamma.shape != (x.shape[1],):
+        raise ValueError("x, res must be (rows, H) and gamma (H,)")
+    rows, H = x.shape
+    h = np.empty_like(x)
+    y = np.empty_like(x)
+    rstd = np.empty(rows)
+    _load().oracle_add_rmsnorm(rows, H, _ptr(x), _ptr(res), _ptr(gamma), float(eps),
+                               _ptr(h), _ptr(y), _ptr(rstd))
+    return h, y, rstd

@@ -17,6 +17,7 @@
  *  [SWIGLU]  "Write a Triton SiLU-Mul (SwiGLU) Kernel"
  *  [LIGER]   "Kernel Profile: SwiGLU (Tier 1 -- Element-wise)" (Liger-Kernel)
  *  [FUSED]   "Fused Kernels" (lesson 5)
+ *  [RMSNORM] "Write a Triton Fused Add+RMSNorm Kernel"
  *
  * Readings where the pages leave a step open (all pinned by tests):
  *  - GELU-erf is evaluated as 0.5*x*erfc(-x/sqrt2), which equals the pages'
@@ -171,6 +172,35 @@ void oracle_bwd(int kind, int64_t n, const double *a, const double *b, const dou
         double x = a[i];
         da[i] = dy[i] * oracle_dact(kind, x) * b[i];
         db[i] = dy[i] * oracle_act(kind, x);
+    }
+}
+
+/* Fused residual add + RMSNorm forward, one row of H values at a time
+ * ([RMSNORM] "Required reasoning process", steps 1-7, and "Correctness
+ * requirements"):
+ *   h = x + residual,  rstd = 1 / sqrt(sum_j h_j^2 / H + eps),
+ *   y = h * rstd * gamma_j   (gamma indexed by column only),
+ * with the mean over all H columns, eps inside the square root, no mean
+ * subtraction and no bias.  h, y: rows*H values; rstd: rows values or NULL.
+ * Statistics and y use the exact sum h (the reading of the single-pass form,
+ * where h stays in fp32 registers), not h rounded to the storage dtype. */
+void oracle_add_rmsnorm(int64_t rows, int64_t H, const double *x, const double *res,
+                        const double *gamma, double eps, double *h, double *y, double *rstd)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        const double *xi = x + i * H, *ri = res + i * H;
+        double *hi = h + i * H, *yi = y + i * H;
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            hi[j] = xi[j] + ri[j];
+            ss += hi[j] * hi[j];
+        }
+        double rs = 1.0 / sqrt(ss / (double)H + eps);
+        for (int64_t j = 0; j < H; ++j)
+            yi[j] = hi[j] * rs * gamma[j];
+        if (rstd)
+            rstd[i] = rs;
     }
 }
 
