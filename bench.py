@@ -41,30 +41,32 @@ KERNEL_SOURCES = ["mlp_gated_activation_amd/csrc/glu_kernels.hip",
                   "mlp_gated_activation_amd/csrc/glu_taylor.h",
                   "mlp_gated_activation_amd/csrc/glu_erfc.h"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_glu_swiglu_bf16_4096x14336.md")
+RMS_SOURCES = ["mlp_gated_activation_amd/csrc/rmsnorm_kernels.hip", "mlp_gated_activation_amd/csrc/rmsnorm_internal.h"]
+RMS_PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_add_rmsnorm_bf16_4096x{h}.md")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
-    """HBM bytes per backward launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources; else None."""
+def committed_traffic(path=PMC_SUMMARY, key="bwd_traffic_bytes", sources=KERNEL_SOURCES):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
     try:
-        text = open(PMC_SUMMARY).read()
+        text = open(path).read()
     except OSError:
         return None
     m = re.search(r"```json\n(.*?)\n```", text, re.S)
     if not m:
         return None
     d = json.loads(m.group(1))
-    if d.get("source_hash") != kernel_source_hash():
+    if d.get("source_hash") != kernel_source_hash(sources):
         return None
-    return d.get("bwd_traffic_bytes")
+    return d.get(key)
 
 
 def cpu_baseline(a, b, dy):
@@ -101,6 +103,10 @@ def cpu_baseline(a, b, dy):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--op", choices=["glu", "add_rmsnorm"], default="glu",
+                    help="glu: the SwiGLU fwd+bwd step (default); add_rmsnorm: the fused residual "
+                         "add + RMSNorm forward, bf16, 4096 rows")
+    ap.add_argument("--hidden", type=int, default=4096, help="add_rmsnorm only: row width")
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets (470 MB each)")
@@ -129,6 +135,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.op == "add_rmsnorm":
+        return bench_add_rmsnorm(args, torch, glu, inputs, dev)
     w = inputs.WORKLOADS["swiglu_bf16_4096x14336"]
     a_h, b_h, dy_h = w.make(seed=0)
     sets = []
@@ -195,6 +203,8 @@ def main():
             b_ = b.detach().requires_grad_()
             (F.silu(a_) * b_).backward(dy)
 
+        for i in range(5):
+            eager_step(i)
         t_ef = timed(eager_fwd, reps) / reps
         t_es = timed(eager_step, reps) / reps
         eager = {"fwd_us": round(1e3 * t_ef, 2), "fwd_GBps": round(FWD_BYTES / (t_ef * 1e-3) / 1e9, 1),
@@ -267,6 +277,94 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(a_h, b_h, dy_h)
+    print(json.dumps(result), flush=True)
+
+
+def bench_add_rmsnorm(args, torch, glu, inputs, dev):
+    """The fused residual add + RMSNorm forward ("Write a Triton Fused
+    Add+RMSNorm Kernel"): bf16 x, residual (4096, H), gamma (H,), eps 1e-6;
+    h and y written out of place, rstd not saved (the inference step).
+    Algorithmic bytes: read x, residual, write h, y = 4*R*H*2, plus gamma once."""
+    R, H = 4096, args.hidden
+    step_bytes = 4 * R * H * 2 + H * 2
+    x_h, r_h, g_h = inputs.add_rmsnorm(R, H, "bf16", seed=0)
+    nsets = max(4, -(-2_000_000_000 // (4 * R * H * 2)))
+    sets = [[x_h.to(dev), r_h.to(dev), torch.empty(R, H, dtype=torch.bfloat16, device=dev),
+             torch.empty(R, H, dtype=torch.bfloat16, device=dev)] for _ in range(nsets)]
+    gamma = g_h.to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        x, r, h, y = sets[i % nsets]
+        glu.glu_add_rmsnorm_fwd(x, r, gamma, 1e-6, h=h, y=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    eager = None
+    if args.torch_eager:
+        import torch.nn.functional as F
+        reps = min(args.steps, 100)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        for i in range(5):   # first calls pay one-time costs
+            F.rms_norm(sets[i % nsets][0] + sets[i % nsets][1], (H,), weight=gamma, eps=1e-6)
+        torch.cuda.synchronize()
+        c0.record(stream)
+        for i in range(reps):
+            x, r, h, y = sets[i % nsets]
+            hh = x + r
+            F.rms_norm(hh, (H,), weight=gamma, eps=1e-6)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        te = c0.elapsed_time(c1) / reps
+        eager = {"us": round(1e3 * te, 2), "GBps": round(step_bytes / (te * 1e-3) / 1e9, 1),
+                 "speedup": round(te / ms, 2), "note": "x + residual, then F.rms_norm, bf16; algorithmic bytes / time"}
+
+    src = [p for p in RMS_SOURCES]
+    traffic = committed_traffic(RMS_PMC_SUMMARY.format(h=H), "traffic_bytes", src)
+    result = {
+        "metric": f"achieved HBM GB/s (% of peak) for bf16 fused residual add + RMSNorm fwd at 4096x{H}",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": f"synthetic (seeded x, residual ~ N(0,1), gamma ~ 1 + 0.1 N(0,1), bf16; {nsets} rotating sets)",
+        "config": {"workload": f"fused residual add + RMSNorm forward, bf16 (4096, {H}), eps 1e-6, h and y out of place",
+                   "rows": R, "hidden": H, "bytes_per_step": step_bytes,
+                   "math": "fp32 sum and statistics in registers, one RNE rounding per output"},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "torch_eager": eager,
+        "roofline": {"bound": "hbm", "kernel": "add_rmsnorm_kernel<bf16>", "achieved": round(value, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    del sets
+    if not args.no_cpu_baseline:
+        import oracle
+        fx, fr, fg = (t.to(torch.float64).numpy() for t in (x_h, r_h, g_h))
+        oracle.add_rmsnorm(fx[:8], fr[:8], fg, 1e-6)
+        times = []
+        t_all = time.perf_counter()
+        while len(times) < 5 and time.perf_counter() - t_all < 10.0:
+            t0 = time.perf_counter()
+            oracle.add_rmsnorm(fx, fr, fg, 1e-6)
+            times.append(time.perf_counter() - t0)
+        best = min(times)
+        result["cpu_baseline"] = {"value": round(step_bytes / best / 1e9, 3), "unit": "GB/s",
+                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "sample": f"full workload (4096x{H}, fp64 scalar C, OpenMP), best of {len(times)}",
+                                  "seconds_per_step": round(best, 4)}
     print(json.dumps(result), flush=True)
 
 

@@ -83,7 +83,8 @@ typedef enum {
     GLU_ERR_ENUM = 4,    /* kind, layout or dtype out of range                      */
     GLU_ERR_ALIAS = 5,   /* an output overlaps an input other than exactly, or another output */
     GLU_ERR_INPLACE = 6, /* inplace not 0/1, or output pointers given with inplace = 1 */
-    GLU_ERR_HIP = 7      /* the kernel launch returned a HIP error                  */
+    GLU_ERR_HIP = 7,     /* the kernel launch returned a HIP error                  */
+    GLU_ERR_ARG = 8      /* a scalar argument out of range (eps must be finite and > 0) */
 } glu_status;
 
 /*
@@ -133,6 +134,34 @@ GLU_API glu_status glu_bwd(glu_kind kind, glu_layout layout, glu_dtype dtype,
                    void *da, int64_t ldda,
                    void *db, int64_t lddb,
                    int inplace, hipStream_t stream);
+
+/*
+ * Fused residual add + RMSNorm forward, one row of `hidden` values at a time
+ * ("Write a Triton Fused Add+RMSNorm Kernel", Required reasoning process,
+ * steps 1-7, and Correctness requirements):
+ *   h = x + residual                      (written back: the next residual)
+ *   rstd = 1 / sqrt(sum_j h_j^2 / hidden + eps)
+ *   y = h * rstd * gamma_j
+ * x, residual, h, y: (rows, hidden) with row strides ldx, ldr, ldh, ldy;
+ * gamma: (hidden,), contiguous; all of `dtype`.  rstd: (rows,) fp32, or NULL
+ * when not needed (training saves it).  eps must be finite and > 0
+ * (GLU_ERR_ARG otherwise); it sits inside the square root and the mean
+ * divides by `hidden`.  The sum is kept unrounded (fp32 for bf16/fp16, fp64
+ * for fp32) for the statistics and y; h is rounded once when stored.
+ * h may be exactly x or exactly residual (in-place residual update) and y
+ * may be exactly x or residual; h and y must not overlap each other, gamma,
+ * rstd, or any input other than exactly.  Rows wider than the kernels'
+ * register capacity (65536 bf16/fp16 or 32768 fp32 values on the aligned
+ * path) are processed in two passes that re-read x and residual; there h
+ * may not overlap x or residual (GLU_ERR_ALIAS).  Forward only.
+ */
+GLU_API glu_status glu_add_rmsnorm_fwd(glu_dtype dtype, int64_t rows, int64_t hidden,
+                               const void *x, int64_t ldx,
+                               const void *residual, int64_t ldr,
+                               const void *gamma,
+                               void *h, int64_t ldh,
+                               void *y, int64_t ldy,
+                               float *rstd, float eps, hipStream_t stream);
 
 /* Static, NUL-terminated English text for a status code (never NULL). */
 GLU_API const char *glu_status_string(glu_status status);

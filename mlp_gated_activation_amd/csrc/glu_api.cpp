@@ -7,10 +7,12 @@
 //   [LIGER]  "Kernel Profile: SwiGLU (Tier 1 -- Element-wise)"
 #include "glu.h"
 
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
 #include "glu_internal.h"
+#include "rmsnorm_internal.h"
 
 namespace {
 
@@ -336,6 +338,85 @@ glu_status glu_bwd(glu_kind kind, glu_layout layout, glu_dtype dtype, int64_t ro
     return enqueue(dtype, kind, true, rows, cols, p, vec, stream);
 }
 
+glu_status glu_add_rmsnorm_fwd(glu_dtype dtype, int64_t rows, int64_t hidden, const void *x, int64_t ldx,
+                               const void *residual, int64_t ldr, const void *gamma, void *h, int64_t ldh,
+                               void *y, int64_t ldy, float *rstd, float eps, hipStream_t stream)
+{
+    if (!(dtype >= GLU_F32 && dtype <= GLU_BF16))
+        return GLU_ERR_ENUM;
+    if (rows < 0 || hidden < 0)
+        return GLU_ERR_SHAPE;
+    if (!(eps > 0.0f) || !isfinite(eps))
+        return GLU_ERR_ARG;
+    if (rows == 0 || hidden == 0)
+        return GLU_OK;
+    if (rows > INT32_MAX || hidden > (int64_t(1) << 31))
+        return GLU_ERR_SHAPE;
+    if (x == nullptr || residual == nullptr || gamma == nullptr || h == nullptr || y == nullptr)
+        return GLU_ERR_NULL;
+    if (ldx < hidden || ldr < hidden || ldh < hidden || ldy < hidden)
+        return GLU_ERR_STRIDE;
+    const int es = glu::elem_size(dtype);
+    const Region rx{uintptr_t(x), ldx, hidden}, rr{uintptr_t(residual), ldr, hidden};
+    const Region rh{uintptr_t(h), ldh, hidden}, ry{uintptr_t(y), ldy, hidden};
+    const Region rg{uintptr_t(gamma), hidden, hidden};
+    int64_t ext;
+    for (const Region *r : {&rx, &rr, &rh, &ry})
+        if (!extent_bytes(rows, *r, es, &ext))
+            return GLU_ERR_SHAPE;
+    if (!extent_bytes(1, rg, es, &ext))
+        return GLU_ERR_SHAPE;
+    // outputs: exactly an input, or disjoint from every input; never each other
+    const Region ins[2] = {rx, rr};
+    if (bad_alias(rows, rh, ins, 2, es) || bad_alias(rows, ry, ins, 2, es))
+        return GLU_ERR_ALIAS;
+    if (overlaps(rows, rh, ry, es))
+        return GLU_ERR_ALIAS;
+    // gamma (one row) against the outputs: compare byte extents
+    auto disjoint = [](uintptr_t a, int64_t na, uintptr_t b, int64_t nb) {
+        return a + uintptr_t(na) <= b || b + uintptr_t(nb) <= a;
+    };
+    int64_t eh, ey;
+    extent_bytes(rows, rh, es, &eh);
+    extent_bytes(rows, ry, es, &ey);
+    const int64_t eg = hidden * es;
+    if (!disjoint(rg.p, eg, rh.p, eh) || !disjoint(rg.p, eg, ry.p, ey))
+        return GLU_ERR_ALIAS;
+    if (rstd != nullptr) {
+        const uintptr_t rp = uintptr_t(rstd);
+        const int64_t rn = rows * int64_t(sizeof(float));
+        int64_t ex2, er2;
+        extent_bytes(rows, rx, es, &ex2);
+        extent_bytes(rows, rr, es, &er2);
+        if (!disjoint(rp, rn, rx.p, ex2) || !disjoint(rp, rn, rr.p, er2) || !disjoint(rp, rn, rg.p, eg) ||
+            !disjoint(rp, rn, rh.p, eh) || !disjoint(rp, rn, ry.p, ey))
+            return GLU_ERR_ALIAS;
+    }
+    const Region all[5] = {rx, rr, rh, ry, rg};
+    bool vec = true;
+    for (const Region &r : all)
+        if (!aligned16(r.p) || (rows > 1 && ((r.ld * es) & 15) != 0))
+            vec = false;
+    const glu::RmsShape shape = glu::rms_shape(hidden, vec ? glu::vec_elems(dtype) : 1);
+    if (shape.vpt == 0 && (overlaps(rows, rh, rx, es) || overlaps(rows, rh, rr, es)))
+        return GLU_ERR_ALIAS;   // the two-pass kernel re-reads x and residual
+    glu::RmsArgs p{};
+    p.x = x;
+    p.res = residual;
+    p.gamma = gamma;
+    p.h = h;
+    p.y = y;
+    p.rstd = rstd;
+    p.ldx = ldx;
+    p.ldr = ldr;
+    p.ldh = ldh;
+    p.ldy = ldy;
+    p.hidden = uint32_t(hidden);
+    p.eps = eps;
+    return glu::launch_add_rmsnorm(dtype, vec, shape, uint32_t(rows), p, stream) == hipSuccess ? GLU_OK
+                                                                                                : GLU_ERR_HIP;
+}
+
 const char *glu_status_string(glu_status status)
 {
     switch (status) {
@@ -347,6 +428,7 @@ const char *glu_status_string(glu_status status)
     case GLU_ERR_ALIAS: return "an output partially overlaps an input or another output";
     case GLU_ERR_INPLACE: return "inplace must be 0 or 1, and output pointers must be NULL when it is 1";
     case GLU_ERR_HIP: return "the HIP kernel launch failed";
+    case GLU_ERR_ARG: return "a scalar argument is out of range (eps must be finite and > 0)";
     }
     return "unknown status";
 }

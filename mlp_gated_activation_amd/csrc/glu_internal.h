@@ -88,6 +88,7 @@ struct Args {
 
 enum Dtype { F32 = 0, F16 = 1, BF16 = 2 };
 
+
 // Enqueues one launch; returns the HIP status of hipLaunchKernel.
 hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args,
                   hipStream_t stream);

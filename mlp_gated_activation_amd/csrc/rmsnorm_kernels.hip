@@ -1,0 +1,348 @@
+// rmsnorm_kernels.hip -- gfx950 kernels for the fused residual add + RMSNorm
+// forward ("Write a Triton Fused Add+RMSNorm Kernel"):
+//   h = x + residual (written back),  rstd = 1/sqrt(mean(h^2) + eps),
+//   y = h * rstd * gamma.
+//
+// One workgroup owns one row (Required reasoning process, step 1).  Every
+// thread loads its 16-byte vectors of x, residual and gamma first, forms h in
+// fp32 registers (fp64 for fp32 data; step 3), stores h rounded to the storage
+// dtype right away (step 4, Kernel design rules), and accumulates sum(h^2).
+// The row sum is reduced in a fixed order (wave shuffles, then LDS across the
+// waves), rstd is formed once per row (step 5, eps inside the square root,
+// denominator H), and y = h * rstd * gamma is stored from the registers
+// (steps 6-7): one pass over HBM, 4*H*s bytes per row plus gamma.  Rows wider
+// than the register capacity use a two-pass kernel that recomputes h from x
+// and residual (step 8, the recompute variant), keeping the arithmetic
+// identical.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "glu_internal.h"
+#include "rmsnorm_internal.h"
+
+namespace glu {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// vector element -> scalar before any bit_cast (this clang miscompiles
+// __builtin_bit_cast applied directly to an ext_vector element)
+__device__ inline uint32_t word(u32x4 v, int j)
+{
+    uint32_t w = v[j];
+    return w;
+}
+
+struct RBf16 {
+    using M = float;
+    static constexpr int VE = 8, SIZE = 2;
+    __device__ static void unpack(u32x4 v, float *x)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __builtin_bit_cast(float, word(v, j) << 16);
+            x[2 * j + 1] = __builtin_bit_cast(float, word(v, j) & 0xffff0000u);
+        }
+    }
+    __device__ static u32x4 pack(const float *y)
+    {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y[2 * j], y[2 * j + 1]}, bf16x2));
+        return v;
+    }
+    __device__ static float load1(const void *p)
+    {
+        return __builtin_bit_cast(float, uint32_t(*static_cast<const uint16_t *>(p)) << 16);
+    }
+    __device__ static void store1(void *p, float y) { *static_cast<__bf16 *>(p) = static_cast<__bf16>(y); }
+};
+
+struct RF16 {
+    using M = float;
+    static constexpr int VE = 8, SIZE = 2;
+    __device__ static void unpack(u32x4 v, float *x)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x2 t = __builtin_convertvector(__builtin_bit_cast(f16x2, word(v, j)), f32x2);
+            x[2 * j] = t[0];
+            x[2 * j + 1] = t[1];
+        }
+    }
+    __device__ static u32x4 pack(const float *y)
+    {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y[2 * j], y[2 * j + 1]}, f16x2));
+        return v;
+    }
+    __device__ static float load1(const void *p) { return float(*static_cast<const _Float16 *>(p)); }
+    __device__ static void store1(void *p, float y) { *static_cast<_Float16 *>(p) = static_cast<_Float16>(y); }
+};
+
+struct RF32 {
+    using M = double;
+    static constexpr int VE = 4, SIZE = 4;
+    __device__ static void unpack(u32x4 v, double *x)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            x[j] = double(__builtin_bit_cast(float, word(v, j)));
+    }
+    __device__ static u32x4 pack(const double *y)
+    {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __builtin_bit_cast(uint32_t, float(y[j]));
+        return v;
+    }
+    __device__ static double load1(const void *p) { return double(*static_cast<const float *>(p)); }
+    __device__ static void store1(void *p, double y) { *static_cast<float *>(p) = float(y); }
+};
+
+template <typename T> __device__ inline u32x4 ldv(const void *base, int64_t off)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const char *>(base) + off * T::SIZE));
+}
+template <typename T> __device__ inline u32x4 ldv_cached(const void *base, int64_t off)
+{
+    // gamma is shared by every row: a normal (cached) load
+    return *reinterpret_cast<const u32x4 *>(static_cast<const char *>(base) + off * T::SIZE);
+}
+template <typename T> __device__ inline void stv(void *base, int64_t off, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(static_cast<char *>(base) + off * T::SIZE));
+}
+__device__ inline const void *at(const void *b, int64_t off, int size) { return static_cast<const char *>(b) + off * size; }
+__device__ inline void *at(void *b, int64_t off, int size) { return static_cast<char *>(b) + off * size; }
+
+__device__ inline float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ inline double shfl_xor(double v, int m) { return __shfl_xor(v, m, 64); }
+
+// Sum over the workgroup in a fixed order: butterfly within each 64-lane wave,
+// then the wave totals in wave order.  Every thread returns the total.
+template <typename M, int BLOCK> __device__ inline M block_sum(M v, M *lds)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += shfl_xor(v, m);
+    constexpr int NW = BLOCK / 64;
+    if constexpr (NW == 1) {
+        return v;
+    } else {
+        const int w = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0)
+            lds[w] = v;
+        __syncthreads();
+        M t = lds[0];
+#pragma unroll
+        for (int i = 1; i < NW; ++i)
+            t += lds[i];
+        return t;
+    }
+}
+
+template <typename M> __device__ inline M rsqrt_row(M ms, float eps) { return M(1) / sqrt(ms + M(eps)); }
+
+// Single pass: VPT vectors per thread stay in registers between the two
+// phases.  All register arrays are indexed with compile-time indices only
+// (ragged vectors use a guarded, fully unrolled loop), so nothing is demoted
+// to scratch memory.  With 8 vectors per thread gamma is loaded in the
+// second phase (an L2 hit: every row reads the same gamma), halving the
+// registers held across the reduction.
+template <typename T, int BLOCK, int VPT, bool VEC>
+__global__ void __launch_bounds__(BLOCK) add_rmsnorm_kernel(const RmsArgs p)
+{
+    using M = typename T::M;
+    constexpr int VE = VEC ? T::VE : 1;
+    constexpr bool G_EARLY = VPT <= 4;
+    __shared__ M lds[BLOCK / 64];
+    const int64_t row = blockIdx.x;
+    const uint32_t H = p.hidden;
+    const void *xr = at(p.x, row * p.ldx, T::SIZE);
+    const void *rr = at(p.res, row * p.ldr, T::SIZE);
+    void *hr = at(p.h, row * p.ldh, T::SIZE);
+    void *yr = at(p.y, row * p.ldy, T::SIZE);
+
+    M h[VPT][VE];
+    M g[G_EARLY ? VPT : 1][VE];
+    M ss = M(0);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const uint32_t col = (uint32_t(v) * BLOCK + threadIdx.x) * VE;
+        if (VEC && col + VE <= H) {
+            M xv[T::VE], rv[T::VE];
+            T::unpack(ldv<T>(xr, col), xv);
+            T::unpack(ldv<T>(rr, col), rv);
+            if constexpr (G_EARLY)
+                T::unpack(ldv_cached<T>(p.gamma, col), g[v]);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                h[v][e] = xv[e] + rv[e];
+                ss += h[v][e] * h[v][e];
+            }
+            stv<T>(hr, col, T::pack(h[v]));
+        } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                if (col + e < H) {
+                    M xe = T::load1(at(xr, col + e, T::SIZE));
+                    M re = T::load1(at(rr, col + e, T::SIZE));
+                    if constexpr (G_EARLY)
+                        g[v][e] = T::load1(at(p.gamma, col + e, T::SIZE));
+                    h[v][e] = xe + re;
+                    ss += h[v][e] * h[v][e];
+                    T::store1(at(hr, col + e, T::SIZE), h[v][e]);
+                }
+            }
+        }
+    }
+    const M rs = rsqrt_row<M>(block_sum<M, BLOCK>(ss, lds) / M(H), p.eps);
+    if (p.rstd != nullptr && threadIdx.x == 0)
+        p.rstd[row] = float(rs);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const uint32_t col = (uint32_t(v) * BLOCK + threadIdx.x) * VE;
+        if (VEC && col + VE <= H) {
+            M gv[T::VE], yv[T::VE];
+            if constexpr (G_EARLY) {
+#pragma unroll
+                for (int e = 0; e < T::VE; ++e)
+                    gv[e] = g[v][e];
+            } else {
+                T::unpack(ldv_cached<T>(p.gamma, col), gv);
+            }
+#pragma unroll
+            for (int e = 0; e < T::VE; ++e)
+                yv[e] = h[v][e] * rs * gv[e];
+            stv<T>(yr, col, T::pack(yv));
+        } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                if (col + e < H) {
+                    M ge;
+                    if constexpr (G_EARLY)
+                        ge = g[v][e];
+                    else
+                        ge = T::load1(at(p.gamma, col + e, T::SIZE));
+                    T::store1(at(yr, col + e, T::SIZE), h[v][e] * rs * ge);
+                }
+            }
+        }
+    }
+}
+
+// Two passes for rows wider than the register capacity: h is recomputed
+// from x and residual in the second pass (the host guarantees h aliases
+// neither of them).
+template <typename T, int BLOCK, bool VEC>
+__global__ void __launch_bounds__(BLOCK) add_rmsnorm_loop_kernel(const RmsArgs p)
+{
+    using M = typename T::M;
+    constexpr int VE = VEC ? T::VE : 1;
+    __shared__ M lds[BLOCK / 64];
+    const int64_t row = blockIdx.x;
+    const uint32_t H = p.hidden;
+    const void *xr = at(p.x, row * p.ldx, T::SIZE);
+    const void *rr = at(p.res, row * p.ldr, T::SIZE);
+    void *hr = at(p.h, row * p.ldh, T::SIZE);
+    void *yr = at(p.y, row * p.ldy, T::SIZE);
+    M ss = M(0);
+    for (uint32_t col = threadIdx.x * VE; col < H; col += uint32_t(BLOCK) * VE) {
+        M hv[T::VE];
+        if (VEC && col + VE <= H) {
+            M xv[T::VE], rv[T::VE];
+            T::unpack(ldv<T>(xr, col), xv);
+            T::unpack(ldv<T>(rr, col), rv);
+#pragma unroll
+            for (int e = 0; e < T::VE; ++e) {
+                hv[e] = xv[e] + rv[e];
+                ss += hv[e] * hv[e];
+            }
+            stv<T>(hr, col, T::pack(hv));
+        } else {
+            const uint32_t n = H - col < uint32_t(VE) ? H - col : uint32_t(VE);
+            for (uint32_t e = 0; e < n; ++e) {
+                M he = T::load1(at(xr, col + e, T::SIZE)) + T::load1(at(rr, col + e, T::SIZE));
+                ss += he * he;
+                T::store1(at(hr, col + e, T::SIZE), he);
+            }
+        }
+    }
+    const M rs = rsqrt_row<M>(block_sum<M, BLOCK>(ss, lds) / M(H), p.eps);
+    if (p.rstd != nullptr && threadIdx.x == 0)
+        p.rstd[row] = float(rs);
+    for (uint32_t col = threadIdx.x * VE; col < H; col += uint32_t(BLOCK) * VE) {
+        if (VEC && col + VE <= H) {
+            M xv[T::VE], rv[T::VE], gv[T::VE], yv[T::VE];
+            T::unpack(ldv<T>(xr, col), xv);
+            T::unpack(ldv<T>(rr, col), rv);
+            T::unpack(ldv_cached<T>(p.gamma, col), gv);
+#pragma unroll
+            for (int e = 0; e < T::VE; ++e)
+                yv[e] = (xv[e] + rv[e]) * rs * gv[e];
+            stv<T>(yr, col, T::pack(yv));
+        } else {
+            const uint32_t n = H - col < uint32_t(VE) ? H - col : uint32_t(VE);
+            for (uint32_t e = 0; e < n; ++e) {
+                M he = T::load1(at(xr, col + e, T::SIZE)) + T::load1(at(rr, col + e, T::SIZE));
+                T::store1(at(yr, col + e, T::SIZE), he * rs * T::load1(at(p.gamma, col + e, T::SIZE)));
+            }
+        }
+    }
+}
+
+typedef void (*RmsFn)(const RmsArgs);
+
+template <typename T, bool VEC> RmsFn pick_rms(RmsShape s)
+{
+    if (s.vpt == 0)
+        return &add_rmsnorm_loop_kernel<T, kRmsLoopBlock, VEC>;
+    switch (s.block * 16 + s.vpt) {
+    case 64 * 16 + 1: return &add_rmsnorm_kernel<T, 64, 1, VEC>;
+    case 64 * 16 + 2: return &add_rmsnorm_kernel<T, 64, 2, VEC>;
+    case 64 * 16 + 4: return &add_rmsnorm_kernel<T, 64, 4, VEC>;
+    case 64 * 16 + 8: return &add_rmsnorm_kernel<T, 64, 8, VEC>;
+    case 128 * 16 + 4: return &add_rmsnorm_kernel<T, 128, 4, VEC>;
+    case 128 * 16 + 8: return &add_rmsnorm_kernel<T, 128, 8, VEC>;
+    case 512 * 16 + 4: return &add_rmsnorm_kernel<T, 512, 4, VEC>;
+    case 1024 * 16 + 4: return &add_rmsnorm_kernel<T, 1024, 4, VEC>;
+    case 128 * 16 + 1: return &add_rmsnorm_kernel<T, 128, 1, VEC>;
+    case 256 * 16 + 1: return &add_rmsnorm_kernel<T, 256, 1, VEC>;
+    case 256 * 16 + 2: return &add_rmsnorm_kernel<T, 256, 2, VEC>;
+    case 256 * 16 + 4: return &add_rmsnorm_kernel<T, 256, 4, VEC>;
+    case 256 * 16 + 8: return &add_rmsnorm_kernel<T, 256, 8, VEC>;
+    case 512 * 16 + 8: return &add_rmsnorm_kernel<T, 512, 8, VEC>;
+    case 1024 * 16 + 8: return &add_rmsnorm_kernel<T, 1024, 8, VEC>;
+    }
+    return nullptr;
+}
+
+template <typename T> RmsFn pick_rms_vec(bool vec, RmsShape s)
+{
+    return vec ? pick_rms<T, true>(s) : pick_rms<T, false>(s);
+}
+
+}  // namespace
+
+hipError_t launch_add_rmsnorm(int dtype, bool vec, RmsShape shape, uint32_t rows, const RmsArgs &args,
+                              hipStream_t stream)
+{
+    RmsFn fn = dtype == F32 ? pick_rms_vec<RF32>(vec, shape)
+             : dtype == F16 ? pick_rms_vec<RF16>(vec, shape)
+                            : pick_rms_vec<RBf16>(vec, shape);
+    if (fn == nullptr)
+        return hipErrorInvalidConfiguration;
+    RmsArgs copy = args;
+    void *kargs[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(rows), dim3(shape.block), kargs, 0, stream);
+}
+
+}  // namespace glu

@@ -31,6 +31,9 @@ _lib.glu_fwd.argtypes = [_i, _i, _i, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _
 _lib.glu_fwd.restype = _i
 _lib.glu_bwd.argtypes = [_i, _i, _i, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i, _p]
 _lib.glu_bwd.restype = _i
+_lib.glu_add_rmsnorm_fwd.argtypes = [_i, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p,
+                                     ctypes.c_float, _p]
+_lib.glu_add_rmsnorm_fwd.restype = _i
 _lib.glu_status_string.argtypes = [_i]
 _lib.glu_status_string.restype = ctypes.c_char_p
 _lib.glu_version.argtypes = []
@@ -40,7 +43,7 @@ KINDS = {"silu": 0, "gelu_erf": 1, "gelu_tanh": 2, "relu": 3}
 LAYOUTS = {"separate": 0, "gate_up": 1}
 DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 STATUS = {0: "GLU_OK", 1: "GLU_ERR_NULL", 2: "GLU_ERR_SHAPE", 3: "GLU_ERR_STRIDE", 4: "GLU_ERR_ENUM",
-          5: "GLU_ERR_ALIAS", 6: "GLU_ERR_INPLACE", 7: "GLU_ERR_HIP"}
+          5: "GLU_ERR_ALIAS", 6: "GLU_ERR_INPLACE", 7: "GLU_ERR_HIP", 8: "GLU_ERR_ARG"}
 
 
 class GluError(RuntimeError):
@@ -221,3 +224,47 @@ def glu_bwd(kind: str, layout: str, a: torch.Tensor, b: torch.Tensor | None, dy:
     if st != 0:
         raise GluError(st, "glu_bwd")
     return result
+
+
+def glu_add_rmsnorm_fwd(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                        h: torch.Tensor | None = None, y: torch.Tensor | None = None, rstd=False,
+                        stream=None):
+    """Fused residual add + RMSNorm forward over the last dimension.
+
+    h = x + residual (allocated if None; pass h=x or h=residual to update the
+    residual stream in place), y = h * rstd * gamma (allocated if None),
+    rstd = 1/sqrt(mean(h^2) + eps) per row: with rstd=True a float32 tensor
+    of the leading shape is allocated and returned, a float32 tensor may be
+    passed instead, and rstd=False skips it.  Returns (h, y, rstd or None).
+    ("Write a Triton Fused Add+RMSNorm Kernel", Required reasoning process.)
+    """
+    dt = _code(DTYPES, x.dtype, "dtype")
+    if x.device.type != "cuda":
+        raise ValueError("tensors must be on a ROCm (cuda) device")
+    if residual.shape != x.shape:
+        raise ValueError(f"residual{tuple(residual.shape)} differs from x{tuple(x.shape)}")
+    hidden = x.shape[-1]
+    if gamma.shape != (hidden,) or (hidden > 1 and gamma.stride(0) != 1):
+        raise ValueError(f"gamma must be a contiguous ({hidden},) tensor")
+    h = torch.empty_like(x) if h is None else h
+    y = torch.empty_like(x) if y is None else y
+    if h.shape != x.shape or y.shape != x.shape:
+        raise ValueError("h and y must have x's shape")
+    _check([("residual", residual), ("gamma", gamma), ("h", h), ("y", y)], x.dtype, x.device)
+    lead = x.shape[:-1]
+    if rstd is True:
+        rstd = torch.empty(lead, dtype=torch.float32, device=x.device)
+    elif rstd is False or rstd is None:
+        rstd = None
+    if rstd is not None and (rstd.dtype != torch.float32 or rstd.numel() != x.numel() // max(hidden, 1)
+                             or not rstd.is_contiguous()):
+        raise ValueError("rstd must be a contiguous float32 tensor with one value per row")
+    x2, r2, h2, y2 = (_rows(t, n) for t, n in ((x, "x"), (residual, "residual"), (h, "h"), (y, "y")))
+    rows = x2.shape[0] if x.dim() > 0 else 0
+    with torch.cuda.device(x.device):
+        st = _lib.glu_add_rmsnorm_fwd(dt, rows, hidden, _ptr(x2), _ld(x2), _ptr(r2), _ld(r2), _ptr(gamma),
+                                      _ptr(h2), _ld(h2), _ptr(y2), _ld(y2), _ptr(rstd), float(eps),
+                                      _stream(x.device, stream))
+    if st != 0:
+        raise GluError(st, "glu_add_rmsnorm_fwd")
+    return h, y, rstd

@@ -79,6 +79,20 @@ def gate_up_stress(rows: int, cols: int, dtype: str, frac: float = 0.01,
     return x, dy
 
 
+def add_rmsnorm(rows: int, hidden: int, dtype: str, seed: int = 0):
+    """x, residual of shape (rows, hidden) and gamma (hidden,) for the fused
+    residual add + RMSNorm ("Write a Triton Fused Add+RMSNorm Kernel").
+
+    Draw order: ``x = randn``, ``residual = randn``, ``gamma = 1 + 0.1*randn``.
+    """
+    g = _gen(seed)
+    t = DTYPES[dtype]
+    x = torch.randn(rows, hidden, generator=g).to(t)
+    res = torch.randn(rows, hidden, generator=g).to(t)
+    gamma = (1.0 + 0.1 * torch.randn(hidden, generator=g)).to(t)
+    return x, res, gamma
+
+
 def all_bit_patterns(dtype: str) -> torch.Tensor:
     """Every 16-bit pattern of a 16-bit dtype, in bit order, as a 1-D tensor."""
     t = DTYPES[dtype]

@@ -21,7 +21,7 @@ ensure_built()
 from mlp_gated_activation_amd import glu  # noqa: E402
 lib = glu._lib
 
-OK, NULL, SHAPE, STRIDE, ENUM, ALIAS, INPLACE, HIP = range(8)
+OK, NULL, SHAPE, STRIDE, ENUM, ALIAS, INPLACE, HIP, ARG = range(9)
 P = 0x7f0000000000          # fake device addresses: validation never dereferences them
 S, GU = 0, 1
 F32, F16, BF16 = 0, 1, 2
@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declarations_are_exported():
     names = declared_functions()
-    assert set(names) == {"glu_fwd", "glu_bwd", "glu_status_string", "glu_version"}
+    assert set(names) == {"glu_fwd", "glu_bwd", "glu_add_rmsnorm_fwd", "glu_status_string", "glu_version"}
     nm = subprocess.run(["nm", "-D", "--defined-only", glu.library_path()],
                         capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in nm.splitlines() if " T " in l}
@@ -43,7 +43,7 @@ def test_header_declarations_are_exported():
 
 def test_version_and_status_strings():
     assert glu.version() >> 16 == 1
-    for s in range(8):
+    for s in range(9):
         assert len(glu.status_string(s)) > 5
     assert glu.status_string(99) == "unknown status"
 
@@ -100,6 +100,30 @@ def test_bwd_rejects(args, want):
     assert bwd(**args) == want
 
 
+def rms(dtype=BF16, rows=4, hidden=64, x=P, ldx=64, r=P + (1 << 20), ldr=64, g=P + (2 << 20),
+        h=P + (3 << 20), ldh=64, y=P + (4 << 20), ldy=64, rstd=P + (5 << 20), eps=1e-6):
+    return lib.glu_add_rmsnorm_fwd(dtype, rows, hidden, x, ldx, r, ldr, g, h, ldh, y, ldy, rstd, eps, None)
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(dtype=3), ENUM), (dict(rows=-1), SHAPE), (dict(hidden=-1), SHAPE),
+    (dict(eps=0.0), ARG), (dict(eps=-1e-6), ARG), (dict(eps=float("inf")), ARG), (dict(eps=float("nan")), ARG),
+    (dict(rows=0, x=None, r=None, g=None, h=None, y=None), OK),
+    (dict(rows=1 << 31), SHAPE), (dict(hidden=(1 << 31) + 1, ldx=1 << 32, ldr=1 << 32, ldh=1 << 32, ldy=1 << 32), SHAPE),
+    (dict(x=None), NULL), (dict(r=None), NULL), (dict(g=None), NULL), (dict(h=None), NULL), (dict(y=None), NULL),
+    (dict(ldx=63), STRIDE), (dict(ldr=1), STRIDE), (dict(ldh=0), STRIDE), (dict(ldy=60), STRIDE),
+    (dict(h=P + 2), ALIAS),                              # h straddles x
+    (dict(y=P + (1 << 20) + 64), ALIAS),                 # y overlaps residual partially
+    (dict(h=P + (4 << 20)), ALIAS),                      # h == y: two outputs
+    (dict(y=P + (2 << 20) - 64), ALIAS),                 # y runs into gamma
+    (dict(rstd=P + 64), ALIAS),                          # rstd inside x
+    (dict(rstd=P + (4 << 20) + 4), ALIAS),               # rstd inside y
+    (dict(hidden=70000, ldx=70000, ldr=70000, ldh=70000, ldy=70000, h=P), ALIAS),  # two-pass: h over x
+])
+def test_add_rmsnorm_rejects(args, want):
+    assert rms(**args) == want
+
+
 def _compile_host(src: str, tmp: str) -> str:
     exe = os.path.join(tmp, "t")
     subprocess.run(["g++", "-O2", "-std=c++17", "-D__HIP_PLATFORM_AMD__", f"-I{CSRC}",
@@ -152,6 +176,12 @@ def test_kernel_isa():
     unroll = int(re.search(r"#define GLU_UNROLL (\d+)", open(os.path.join(CSRC, "glu_internal.h")).read()).group(1))
     starts = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\w*glu_kernel\w*):", asm, re.M)]
     assert len(starts) == 96
+    assert set(re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)) == {"0"}, "a kernel uses scratch"
+    # every kernel of the library: no MFMA, no packed fp32
+    for name in re.findall(r"^(_Z\w+):", asm, re.M):
+        pos = asm.find(name + ":")
+        body = asm[pos:asm.find("s_endpgm", pos)]
+        assert "mfma" not in body and not re.search(r"v_pk_(add|mul|fma)_f32", body), name
     for pos, name in starts:
         body = asm[pos:asm.find("s_endpgm", pos)]
         assert "mfma" not in body, name
@@ -163,3 +193,29 @@ def test_kernel_isa():
         if vec:
             assert len(re.findall("global_load_dwordx4", body)) == unroll * (3 if bwd else 2), name
             assert len(re.findall("global_store_dwordx4", body)) == unroll * (2 if bwd else 1), name
+
+
+@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="needs hipcc")
+def test_rmsnorm_kernel_isa():
+    """The add+RMSNorm kernels: no MFMA or packed fp32, no fp64 outside the
+    fp32-data instances, 16-byte vector I/O on the aligned path."""
+    from mlp_gated_activation_amd import build as b
+    src = [s for s in b.SOURCES if s.endswith("rmsnorm_kernels.hip")][0]
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [b.HIPCC, *[f for f in b.FLAGS if f not in ("-shared",)], f"-I{b.INCLUDE}", f"-I{b.CSRC}",
+               "--save-temps", "-c", src, "-o", os.path.join(tmp, "k.o")]
+        subprocess.run(cmd, cwd=tmp, check=True, capture_output=True)
+        asm = open(os.path.join(tmp, "rmsnorm_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")).read()
+    names = re.findall(r"^(_Z\w*rmsnorm\w*kernel\w*):", asm, re.M)
+    assert len(names) == 3 * 2 * 16   # 15 single-pass shapes + the two-pass kernel
+    # register arrays must stay in registers: no private (scratch) memory
+    assert re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm) and \
+        set(re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)) == {"0"}
+    for name in names:
+        pos = asm.find(name + ":")
+        body = asm[pos:asm.find("s_endpgm", pos)]
+        assert "mfma" not in body and not re.search(r"v_pk_(add|mul|fma)_f32", body), name
+        if "RF32" not in name:
+            assert not re.search(r"^\s+v_\w+_f64", body, re.M), name
+        if re.search(r"ELb1EEEvNS_7RmsArgsE", name):   # VEC instances
+            assert "global_load_dwordx4" in body and "global_store_dwordx4" in body, name
