@@ -103,9 +103,10 @@ def cpu_baseline(a, b, dy):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=["glu", "add_rmsnorm"], default="glu",
+    ap.add_argument("--op", choices=["glu", "add_rmsnorm", "glu_strided"], default="glu",
                     help="glu: the SwiGLU fwd+bwd step (default); add_rmsnorm: the fused residual "
-                         "add + RMSNorm forward, bf16, 4096 rows")
+                         "add + RMSNorm forward, bf16, 4096 rows; glu_strided: the SwiGLU backward "
+                         "with a transposed incoming gradient (LDS-tiled kernel) and related layouts")
     ap.add_argument("--hidden", type=int, default=4096, help="add_rmsnorm only: row width")
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
@@ -137,6 +138,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.op == "add_rmsnorm":
         return bench_add_rmsnorm(args, torch, glu, inputs, dev)
+    if args.op == "glu_strided":
+        return bench_strided(args, torch, glu, inputs, dev)
     w = inputs.WORKLOADS["swiglu_bf16_4096x14336"]
     a_h, b_h, dy_h = w.make(seed=0)
     sets = []
@@ -365,6 +368,90 @@ def bench_add_rmsnorm(args, torch, glu, inputs, dev):
                                   "cores": oracle.num_threads(), "kind": "oracle",
                                   "sample": f"full workload (4096x{H}, fp64 scalar C, OpenMP), best of {len(times)}",
                                   "seconds_per_step": round(best, 4)}
+    print(json.dumps(result), flush=True)
+
+
+def bench_strided(args, torch, glu, inputs, dev):
+    """SwiGLU bf16 (4096, 14336) on strided views, no .contiguous() copies:
+      * bwd_dyT: backward in place with dy a transposed view (column-major)
+        while a, b are row-major: the LDS-tiled kernel (the headline here);
+      * fwd_yT: forward into a transposed output: the LDS-tiled kernel;
+      * all_T: forward + backward with every operand transposed: the
+        streaming kernels on the transposed problem;
+      * copy_then_bwd: what a caller without strided support does,
+        dy.contiguous() then the row-major backward.
+    Algorithmic bytes as in the main step (fwd 3*N*2, bwd 5*N*2)."""
+    w = inputs.WORKLOADS["swiglu_bf16_4096x14336"]
+    a_h, b_h, dy_h = w.make(seed=0)
+    dyT_h = dy_h.t().contiguous()
+    sets = []
+    for _ in range(args.sets):
+        sets.append([a_h.to(dev), b_h.to(dev), dyT_h.to(dev).t(),
+                     torch.empty(COLS, ROWS, dtype=torch.bfloat16, device=dev).t()])
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        for i in range(min(n, args.warmup)):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def bwd_dyT(i):
+        a, b, dyT, yT = sets[i % len(sets)]
+        glu.glu_bwd_strided("silu", a, b, dyT, da=a, db=b)
+
+    def fwd_yT(i):
+        a, b, dyT, yT = sets[i % len(sets)]
+        glu.glu_fwd_strided("silu", a, b, yT)
+
+    def copy_then_bwd(i):
+        a, b, dyT, yT = sets[i % len(sets)]
+        glu.glu_bwd("silu", "separate", a, b, dyT.contiguous(), inplace=True)
+
+    t_bwd = timed(bwd_dyT, args.steps)
+    t_fwd = timed(fwd_yT, args.steps)
+    t_copy = timed(copy_then_bwd, min(args.steps, 200))
+    # every operand transposed: reuse the buffers as (COLS, ROWS) matrices seen transposed
+    tsets = [[s_[0].view(COLS, ROWS).t(), s_[1].view(COLS, ROWS).t(), s_[2], s_[3]] for s_ in sets]
+
+    def all_T(i):
+        aT, bT, dyT, yT = tsets[i % len(tsets)]
+        glu.glu_fwd_strided("silu", aT, bT, yT)
+        glu.glu_bwd_strided("silu", aT, bT, dyT, da=aT, db=bT)
+
+    t_allT = timed(all_T, args.steps)
+    gbs = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 1)
+    value = gbs(BWD_BYTES, t_bwd)
+    result = {
+        "metric": "achieved HBM GB/s (% of peak) for bf16 silu backward, transposed dy view, 4096x14336",
+        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_bwd, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": f"synthetic (seeded as the main step; {args.sets} rotating buffer sets)",
+        "config": {"workload": "SwiGLU bf16 backward in place, a, b row-major (4096, 14336), dy a transposed "
+                               "view (column-major), no copies", "rows": ROWS, "cols": COLS,
+                   "bytes_per_step": BWD_BYTES},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "kernels": {
+            "bwd_dyT": {"avg_us": round(1e3 * t_bwd, 2), "GBps": value, "path": "tiles"},
+            "fwd_yT": {"avg_us": round(1e3 * t_fwd, 2), "GBps": gbs(FWD_BYTES, t_fwd), "path": "tiles"},
+            "all_T_fwd_bwd": {"avg_us": round(1e3 * t_allT, 2), "GBps": gbs(STEP_BYTES, t_allT),
+                              "path": "streaming kernels on the transposed problem"},
+            "copy_then_bwd": {"avg_us": round(1e3 * t_copy, 2), "GBps": gbs(BWD_BYTES, t_copy),
+                              "path": "dy.contiguous() + row-major backward"},
+        },
+        "roofline": {"bound": "hbm", "kernel": "glu_tile_kernel<bf16, silu, bwd>", "achieved": value,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
     print(json.dumps(result), flush=True)
 
 

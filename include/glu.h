@@ -84,7 +84,8 @@ typedef enum {
     GLU_ERR_ALIAS = 5,   /* an output overlaps an input other than exactly, or another output */
     GLU_ERR_INPLACE = 6, /* inplace not 0/1, or output pointers given with inplace = 1 */
     GLU_ERR_HIP = 7,     /* the kernel launch returned a HIP error                  */
-    GLU_ERR_ARG = 8      /* a scalar argument out of range (eps must be finite and > 0) */
+    GLU_ERR_ARG = 8      /* a scalar argument out of range (eps must be finite and > 0), or a
+                            strided operand's pointer not aligned to its element size */
 } glu_status;
 
 /*
@@ -134,6 +135,38 @@ GLU_API glu_status glu_bwd(glu_kind kind, glu_layout layout, glu_dtype dtype,
                    void *da, int64_t ldda,
                    void *db, int64_t lddb,
                    int inplace, hipStream_t stream);
+
+/*
+ * The same forward and backward on operands of any 2-D layout: element
+ * (r, c) of operand t lives at t + r*t_rs + c*t_cs (strides in ELEMENTS,
+ * both >= 0; pointers aligned to the element size), so transposed, sliced
+ * and broadcast (stride 0) views need no copy ("Write a Triton SiLU-Mul
+ * (SwiGLU) Kernel", Kernel design rules and Common failure modes: strides
+ * come from the tensor's metadata, and a transposed view must either be
+ * made contiguous or have its strides threaded through the kernel).  The [gate | up] layout is the two views x and x + cols*cs.
+ *
+ * Outputs (y; da, db) must not map two (r, c) to one address
+ * (GLU_ERR_STRIDE otherwise).  An output may coincide exactly with an input
+ * (same pointer and both strides: the in-place forms); any other overlap of
+ * an output with an input or with the other output is GLU_ERR_ALIAS.
+ * When every operand is row-major (column stride 1) or every operand is
+ * column-major (row stride 1) the 16-byte streaming kernels run; otherwise
+ * 64 x 64 tiles are staged through LDS so each operand is still read or
+ * written along its own contiguous direction.
+ */
+GLU_API glu_status glu_fwd_strided(glu_kind kind, glu_dtype dtype, int64_t rows, int64_t cols,
+                           const void *a, int64_t a_rs, int64_t a_cs,
+                           const void *b, int64_t b_rs, int64_t b_cs,
+                           void *y, int64_t y_rs, int64_t y_cs,
+                           hipStream_t stream);
+
+GLU_API glu_status glu_bwd_strided(glu_kind kind, glu_dtype dtype, int64_t rows, int64_t cols,
+                           const void *a, int64_t a_rs, int64_t a_cs,
+                           const void *b, int64_t b_rs, int64_t b_cs,
+                           const void *dy, int64_t dy_rs, int64_t dy_cs,
+                           void *da, int64_t da_rs, int64_t da_cs,
+                           void *db, int64_t db_rs, int64_t db_cs,
+                           hipStream_t stream);
 
 /*
  * Fused residual add + RMSNorm forward, one row of `hidden` values at a time

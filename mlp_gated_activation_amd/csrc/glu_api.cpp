@@ -199,9 +199,222 @@ bool vec_ok(const Region *r, int n, int es, int64_t rows)
     return true;
 }
 
+// --- strided operands -------------------------------------------------------
+
+struct Op2 {
+    uintptr_t p;
+    int64_t rs, cs;
+};
+
+bool same2(const Op2 &x, const Op2 &y) { return x.p == y.p && x.rs == y.rs && x.cs == y.cs; }
+
+// Byte extent of an operand's elements: [p, p + span); false on overflow.
+bool span2(int64_t rows, int64_t cols, const Op2 &o, int es, int64_t *out)
+{
+    int64_t a, b, s;
+    if (__builtin_mul_overflow(rows - 1, o.rs, &a) || __builtin_mul_overflow(cols - 1, o.cs, &b) ||
+        __builtin_add_overflow(a, b, &s) || __builtin_add_overflow(s, int64_t(1), &s) ||
+        __builtin_mul_overflow(s, int64_t(es), &s))
+        return false;
+    uintptr_t end;
+    if (__builtin_add_overflow(o.p, uintptr_t(s), &end))
+        return false;
+    *out = s;
+    return true;
+}
+
+// (r, c) -> r*rs + c*cs is one-to-one on [0, rows) x [0, cols) (sufficient
+// condition: the larger stride steps over the whole extent of the smaller).
+bool injective(int64_t rows, int64_t cols, const Op2 &o)
+{
+    int64_t s1 = o.rs, n1 = rows, s2 = o.cs, n2 = cols;
+    if (n1 == 1)
+        return n2 == 1 || s2 >= 1;
+    if (n2 == 1)
+        return s1 >= 1;
+    if (s1 > s2) {
+        int64_t t = s1; s1 = s2; s2 = t;
+        t = n1; n1 = n2; n2 = t;
+    }
+    int64_t need;
+    return s1 >= 1 && !__builtin_mul_overflow(s1, n1, &need) && s2 >= need;
+}
+
+// The operand as `n` runs of `width` contiguous elements `ld` apart: row-major
+// (column stride 1) gives rows of cols, column-major (row stride 1) gives
+// columns of rows.  Returns 0 when it is neither, 1 row-major, 2 column-major.
+int as_runs(int64_t rows, int64_t cols, const Op2 &o, int64_t *n, Region *r)
+{
+    if ((cols == 1 || o.cs == 1) && (rows == 1 || o.rs >= cols)) {
+        *n = rows;
+        *r = Region{o.p, rows > 1 ? o.rs : cols, cols};
+        return 1;
+    }
+    if ((rows == 1 || o.rs == 1) && (cols == 1 || o.cs >= rows)) {
+        *n = cols;
+        *r = Region{o.p, cols > 1 ? o.cs : rows, rows};
+        return 2;
+    }
+    return 0;
+}
+
+// True when some element of x and some element of y share a byte.  Exact
+// for two views with the same orientation and leading stride (for example
+// the two halves of [gate | up]); conservative (true) otherwise when the
+// byte extents intersect.
+bool overlap2(int64_t rows, int64_t cols, const Op2 &x, const Op2 &y, int es)
+{
+    int64_t ex = 0, ey = 0;
+    span2(rows, cols, x, es, &ex);
+    span2(rows, cols, y, es, &ey);
+    if (x.p + uintptr_t(ex) <= y.p || y.p + uintptr_t(ey) <= x.p)
+        return false;
+    int64_t nx, ny;
+    Region rx, ry;
+    const int ox = as_runs(rows, cols, x, &nx, &rx), oy = as_runs(rows, cols, y, &ny, &ry);
+    if (ox == 0 || ox != oy)
+        return true;
+    return overlaps(nx, rx, ry, es);
+}
+
+glu_status strided(bool bwd, int kind, int dtype, int64_t rows, int64_t cols, const Op2 *ins, const Op2 *outs,
+                   hipStream_t stream)
+{
+    if (!(kind >= GLU_SILU && kind <= GLU_RELU) || !(dtype >= GLU_F32 && dtype <= GLU_BF16))
+        return GLU_ERR_ENUM;
+    if (rows < 0 || cols < 0)
+        return GLU_ERR_SHAPE;
+    if (rows == 0 || cols == 0)
+        return GLU_OK;
+    const int nin = bwd ? 3 : 2, nout = bwd ? 2 : 1;
+    const int es = glu::elem_size(dtype);
+    for (int i = 0; i < nin + nout; ++i) {
+        const Op2 &o = i < nin ? ins[i] : outs[i - nin];
+        if (o.p == 0)
+            return GLU_ERR_NULL;
+        if (o.rs < 0 || o.cs < 0)
+            return GLU_ERR_STRIDE;
+        if (o.p % uintptr_t(es) != 0)
+            return GLU_ERR_ARG;
+        int64_t ext;
+        if (!span2(rows, cols, o, es, &ext))
+            return GLU_ERR_SHAPE;
+    }
+    for (int k = 0; k < nout; ++k) {
+        if (!injective(rows, cols, outs[k]))
+            return GLU_ERR_STRIDE;
+        for (int i = 0; i < nin; ++i)
+            if (!same2(outs[k], ins[i]) && overlap2(rows, cols, outs[k], ins[i], es))
+                return GLU_ERR_ALIAS;
+    }
+    if (nout == 2 && overlap2(rows, cols, outs[0], outs[1], es))
+        return GLU_ERR_ALIAS;
+
+    // Row-major everywhere (column stride 1, rows apart): the streaming kernels.
+    // Column-major everywhere: the same kernels on the transposed problem.
+    for (int transpose = 0; transpose < 2; ++transpose) {
+        const int64_t R = transpose ? cols : rows, C = transpose ? rows : cols;
+        bool ok = true;
+        Region rin[3], rout[2];
+        for (int i = 0; i < nin + nout; ++i) {
+            const Op2 &o = i < nin ? ins[i] : outs[i - nin];
+            const int64_t unit = transpose ? o.rs : o.cs, ld = transpose ? o.cs : o.rs;
+            if ((C > 1 && unit != 1) || (R > 1 && ld < C))
+                ok = false;
+            const Region r{o.p, R > 1 ? ld : C, C};
+            (i < nin ? rin[i] : rout[i - nin]) = r;
+        }
+        if (!ok)
+            continue;
+        Region all[5];
+        for (int i = 0; i < nin; ++i)
+            all[i] = rin[i];
+        for (int i = 0; i < nout; ++i)
+            all[nin + i] = rout[i];
+        Args p{};
+        p.in0 = reinterpret_cast<const void *>(rin[0].p);
+        p.in1 = reinterpret_cast<const void *>(rin[1].p);
+        p.in2 = bwd ? reinterpret_cast<const void *>(rin[2].p) : nullptr;
+        p.out0 = reinterpret_cast<void *>(rout[0].p);
+        p.out1 = bwd ? reinterpret_cast<void *>(rout[1].p) : nullptr;
+        p.ld_in0 = rin[0].ld;
+        p.ld_in1 = rin[1].ld;
+        p.ld_in2 = bwd ? rin[2].ld : 0;
+        p.ld_out0 = rout[0].ld;
+        p.ld_out1 = bwd ? rout[1].ld : 0;
+        return enqueue(dtype, kind, bwd, R, C, p, vec_ok(all, nin + nout, es, R), stream);
+    }
+
+    // Mixed layouts: 64 x 64 tiles.  The kernel works in row orientation, so
+    // the whole problem is transposed when more operands are contiguous down
+    // the columns than along the rows.
+    int nrow = 0, ncol = 0;
+    for (int i = 0; i < nin + nout; ++i) {
+        const Op2 &o = i < nin ? ins[i] : outs[i - nin];
+        nrow += o.cs == 1;
+        ncol += o.rs == 1;
+    }
+    const bool flip = ncol > nrow;
+    const int64_t R = flip ? cols : rows, C = flip ? rows : cols;
+    const int64_t tr = (R + glu::kTile - 1) / glu::kTile, tc = (C + glu::kTile - 1) / glu::kTile;
+    int64_t ntiles;
+    if (__builtin_mul_overflow(tr, tc, &ntiles) || ntiles > int64_t(UINT32_MAX))
+        return GLU_ERR_SHAPE;
+    auto mode = [&](const Op2 &o, int64_t *rs, int64_t *cs) -> uint8_t {
+        *rs = flip ? o.cs : o.rs;
+        *cs = flip ? o.rs : o.cs;
+        const bool base16 = aligned16(o.p);
+        if (*cs == 1 && base16 && (R <= 1 || ((*rs * es) & 15) == 0))
+            return glu::kDirect;
+        if (*rs == 1 && base16 && (C <= 1 || ((*cs * es) & 15) == 0))
+            return glu::kTransposed;
+        return glu::kGather;
+    };
+    glu::TileArgs t{};
+    for (int i = 0; i < nin; ++i) {
+        t.in[i] = reinterpret_cast<const void *>(ins[i].p);
+        t.in_mode[i] = mode(ins[i], &t.irs[i], &t.ics[i]);
+    }
+    for (int i = 0; i < nout; ++i) {
+        t.out[i] = reinterpret_cast<void *>(outs[i].p);
+        t.out_mode[i] = mode(outs[i], &t.ors[i], &t.ocs[i]);
+    }
+    t.rows = R;
+    t.cols = C;
+    t.tiles_r = uint32_t(tr);
+    t.tiles_c = uint32_t(tc);
+    for (int64_t t0 = 0; t0 < ntiles; t0 += glu::kMaxTilesPerLaunch) {
+        const int64_t n = ntiles - t0 < glu::kMaxTilesPerLaunch ? ntiles - t0 : glu::kMaxTilesPerLaunch;
+        t.tile0 = uint32_t(t0);
+        if (glu::launch_tiles(dtype, kind, bwd, t, uint32_t(n), stream) != hipSuccess)
+            return GLU_ERR_HIP;
+    }
+    return GLU_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+glu_status glu_fwd_strided(glu_kind kind, glu_dtype dtype, int64_t rows, int64_t cols, const void *a, int64_t a_rs,
+                           int64_t a_cs, const void *b, int64_t b_rs, int64_t b_cs, void *y, int64_t y_rs,
+                           int64_t y_cs, hipStream_t stream)
+{
+    const Op2 ins[2] = {{uintptr_t(a), a_rs, a_cs}, {uintptr_t(b), b_rs, b_cs}};
+    const Op2 outs[1] = {{uintptr_t(y), y_rs, y_cs}};
+    return strided(false, kind, dtype, rows, cols, ins, outs, stream);
+}
+
+glu_status glu_bwd_strided(glu_kind kind, glu_dtype dtype, int64_t rows, int64_t cols, const void *a, int64_t a_rs,
+                           int64_t a_cs, const void *b, int64_t b_rs, int64_t b_cs, const void *dy,
+                           int64_t dy_rs, int64_t dy_cs, void *da, int64_t da_rs, int64_t da_cs, void *db,
+                           int64_t db_rs, int64_t db_cs, hipStream_t stream)
+{
+    const Op2 ins[3] = {{uintptr_t(a), a_rs, a_cs}, {uintptr_t(b), b_rs, b_cs}, {uintptr_t(dy), dy_rs, dy_cs}};
+    const Op2 outs[2] = {{uintptr_t(da), da_rs, da_cs}, {uintptr_t(db), db_rs, db_cs}};
+    return strided(true, kind, dtype, rows, cols, ins, outs, stream);
+}
+
 
 glu_status glu_fwd(glu_kind kind, glu_layout layout, glu_dtype dtype, int64_t rows, int64_t cols, void *a,
                    int64_t lda, void *b, int64_t ldb, void *y, int64_t ldy, int inplace, hipStream_t stream)

@@ -89,6 +89,65 @@ struct Args {
 enum Dtype { F32 = 0, F16 = 1, BF16 = 2 };
 
 
+// Strided operands of any layout, processed in 64 x 64 tiles staged through
+// LDS: every operand is read or written along its own contiguous direction.
+constexpr int kTile = 64;
+// How a tiled-kernel operand moves between HBM and registers.
+enum TileMode : uint8_t {
+    kDirect = 0,      // column stride 1, 16-byte aligned: 16-byte chunks along the row
+    kTransposed = 1,  // row stride 1, 16-byte aligned: 16-byte chunks down the column, through LDS
+    kGather = 2,      // anything else (broadcast, sliced, unaligned): element by element
+};
+
+struct TileArgs {
+    const void *in[3];      // a, b, dy
+    void *out[2];           // y | da, db
+    int64_t irs[3], ics[3]; // input row / column strides (elements)
+    int64_t ors[2], ocs[2];
+    int64_t rows, cols;
+    uint32_t tiles_r, tiles_c;
+    uint32_t tile0;         // first tile (in launch order) of this launch
+    uint8_t in_mode[3];     // TileMode per operand
+    uint8_t out_mode[2];
+};
+
+#ifndef GLU_TILE_GROUP
+#define GLU_TILE_GROUP 8
+#endif
+constexpr uint32_t kTileGroup = GLU_TILE_GROUP;
+
+#if defined(__HIPCC__)
+#define GLU_HD __host__ __device__
+#else
+#define GLU_HD
+#endif
+
+// Launch order of the tiles: bands of kTileGroup tile rows, walked column
+// by column inside a band.  The blocks in flight then cover a strip of
+// kTileGroup*64 rows, so row-major operands are read in long runs along
+// each row and column-major ones in runs of kTileGroup*64 elements down each
+// column.  Tile t of the order covers rows [64*r, 64*r + 64) and columns
+// [64*c, 64*c + 64).
+struct TileCoord {
+    uint32_t r, c;
+};
+GLU_HD inline TileCoord tile_coord(uint32_t t, uint32_t tiles_r, uint32_t tiles_c)
+{
+    const uint64_t per_group = uint64_t(kTileGroup) * tiles_c;
+    const uint32_t g = uint32_t(t / per_group);
+    const uint32_t first = g * kTileGroup;
+    const uint32_t h = tiles_r - first < kTileGroup ? tiles_r - first : kTileGroup;
+    const uint64_t in_g = t - uint64_t(g) * per_group;
+    return TileCoord{first + uint32_t(in_g % h), uint32_t(in_g / h)};
+}
+
+// Largest tile count one launch covers.
+// grid * 256 threads must stay below 2^32 work-items per dimension
+constexpr uint32_t kMaxTilesPerLaunch = 1u << 22;
+
+hipError_t launch_tiles(int dtype, int kind, bool backward, const TileArgs &args, uint32_t ntiles,
+                        hipStream_t stream);
+
 // Enqueues one launch; returns the HIP status of hipLaunchKernel.
 hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args,
                   hipStream_t stream);

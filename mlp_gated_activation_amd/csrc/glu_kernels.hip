@@ -456,6 +456,195 @@ __global__ void __launch_bounds__(block_size<BWD>()) glu_kernel(const Args p)
 }
 
 // ---------------------------------------------------------------------------
+// Tiled kernel for strided operands of mixed layouts.  One workgroup of 256
+// threads (4 waves) owns a 64 x 64 tile and computes it in row orientation:
+// thread chunk q = tid + 256*j (j < CPT) is line q / LINE, segment q % LINE,
+// i.e. the VE elements (line, seg*VE + e).
+//  - kDirect operands (column stride 1) move those chunks straight between
+//    HBM and registers as 16-byte vectors;
+//  - kTransposed operands (row stride 1) move 16-byte chunks down a column,
+//    (seg*VE + e, line), and are turned around through LDS: float slots with
+//    a row pitch of 65 words, which is conflict-free both ways;
+//  - kGather operands are read / written element by element.
+// Every load of the tile is issued before any LDS traffic or math.  Values
+// are exact in float (the fp32 data's compute widening to double happens in
+// registers); results are rounded once to the storage type.
+// ---------------------------------------------------------------------------
+template <typename T> __device__ inline void unpack_f(u32x4 v, float *x)
+{
+    if constexpr (T::SIZE == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            x[j] = __builtin_bit_cast(float, word(v, j));
+    } else {
+        T::unpack(v, x);
+    }
+}
+template <typename T> __device__ inline u32x4 pack_f(const float *y)
+{
+    if constexpr (T::SIZE == 4) {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __builtin_bit_cast(uint32_t, y[j]);
+        return v;
+    } else {
+        return T::pack(y);
+    }
+}
+
+template <typename T, int KIND, bool BWD>
+__global__ void __launch_bounds__(256) glu_tile_kernel(const TileArgs p)
+{
+    using M = typename T::M;
+    constexpr int NIN = BWD ? 3 : 2, NOUT = BWD ? 2 : 1;
+    constexpr int VE = T::VE;                             // elements per 16-byte chunk
+    constexpr int LINE = kTile / VE;                      // chunks per tile line
+    constexpr int CPT = kTile * kTile / (256 * VE);       // chunks per thread
+    __shared__ float lds[NIN][kTile][kTile + 1];
+
+    const TileCoord tc = tile_coord(p.tile0 + blockIdx.x, p.tiles_r, p.tiles_c);
+    const int64_t r0 = int64_t(tc.r) * kTile, c0 = int64_t(tc.c) * kTile;
+    const int tid = threadIdx.x;
+
+    // Phase 1: every full 16-byte chunk of every input, all loads in flight.
+    u32x4 raw[NIN][CPT];
+    bool vec[NIN][CPT];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k) {
+        const int mode = p.in_mode[k];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int q = tid + 256 * j, line = q / LINE, seg = q % LINE;
+            const bool tr = mode == kTransposed;
+            const int64_t r = tr ? r0 + seg * VE : r0 + line, c = tr ? c0 + line : c0 + seg * VE;
+            vec[k][j] = mode != kGather && (tr ? (c < p.cols && r + VE <= p.rows) : (r < p.rows && c + VE <= p.cols));
+            if (vec[k][j])
+                raw[k][j] = ldv<T>(p.in[k], r * p.irs[k] + c * p.ics[k]);
+        }
+    }
+    // Unpack, or fetch element by element (gathered operands, ragged edges;
+    // outside the problem: 0).
+    float x[NIN][CPT][VE];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k) {
+        const bool tr = p.in_mode[k] == kTransposed;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            if (vec[k][j]) {
+                unpack_f<T>(raw[k][j], x[k][j]);
+            } else {
+                const int q = tid + 256 * j, line = q / LINE, seg = q % LINE;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    const int64_t r = tr ? r0 + seg * VE + e : r0 + line;
+                    const int64_t c = tr ? c0 + line : c0 + seg * VE + e;
+                    x[k][j][e] = (r < p.rows && c < p.cols)
+                                     ? float(T::load1(at(p.in[k], r * p.irs[k] + c * p.ics[k], T::SIZE)))
+                                     : 0.0f;
+                }
+            }
+        }
+    }
+
+    // Phase 2: turn the transposed inputs around through LDS.
+#pragma unroll
+    for (int k = 0; k < NIN; ++k)
+        if (p.in_mode[k] == kTransposed) {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const int q = tid + 256 * j, line = q / LINE, seg = q % LINE;
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    lds[k][seg * VE + e][line] = x[k][j][e];
+            }
+        }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NIN; ++k)
+        if (p.in_mode[k] == kTransposed) {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const int q = tid + 256 * j, line = q / LINE, seg = q % LINE;
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    x[k][j][e] = lds[k][line][seg * VE + e];
+            }
+        }
+
+    // Phase 3: the math, in row orientation; one rounding per result.
+    float y[NOUT][CPT][VE];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            const M a = M(x[0][j][e]), b = M(x[1][j][e]);
+            if constexpr (!BWD) {
+                y[0][j][e] = float(act<KIND, M>(a) * b);
+            } else {
+                const M dy = M(x[2][j][e]);
+                M f, g;
+                act_grad<KIND, T::PATCH, M>(a, f, g);
+                y[0][j][e] = float((dy * g) * b);
+                y[1][j][e] = float(dy * f);
+            }
+        }
+
+    // Phase 4: transposed outputs go back through LDS, then every output is
+    // stored along its own contiguous direction.
+    __syncthreads();   // phase-2 reads are done before the slots are reused
+#pragma unroll
+    for (int k = 0; k < NOUT; ++k)
+        if (p.out_mode[k] == kTransposed) {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const int q = tid + 256 * j, line = q / LINE, seg = q % LINE;
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    lds[k][line][seg * VE + e] = y[k][j][e];
+            }
+        }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NOUT; ++k) {
+        const int mode = p.out_mode[k];
+        const bool tr = mode == kTransposed;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int q = tid + 256 * j, line = q / LINE, seg = q % LINE;
+            float v[VE];
+#pragma unroll
+            for (int e = 0; e < VE; ++e)
+                v[e] = tr ? lds[k][seg * VE + e][line] : y[k][j][e];
+            const int64_t r = tr ? r0 + seg * VE : r0 + line, c = tr ? c0 + line : c0 + seg * VE;
+            const bool full = mode != kGather && (tr ? (c < p.cols && r + VE <= p.rows) : (r < p.rows && c + VE <= p.cols));
+            if (full) {
+                stv<T>(p.out[k], r * p.ors[k] + c * p.ocs[k], pack_f<T>(v));
+            } else {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    const int64_t rr = tr ? r + e : r, cc = tr ? c : c + e;
+                    if (rr < p.rows && cc < p.cols)
+                        T::store1(at(p.out[k], rr * p.ors[k] + cc * p.ocs[k], T::SIZE), M(v[e]));
+                }
+            }
+        }
+    }
+}
+
+typedef void (*TileFn)(const TileArgs);
+
+template <typename T, bool BWD> TileFn pick_tile(int kind)
+{
+    switch (kind) {
+    case SILU: return &glu_tile_kernel<T, SILU, BWD>;
+    case GELU_ERF: return &glu_tile_kernel<T, GELU_ERF, BWD>;
+    case GELU_TANH: return &glu_tile_kernel<T, GELU_TANH, BWD>;
+    default: return &glu_tile_kernel<T, RELU, BWD>;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Dispatch table: [dtype][kind][backward][vec].
 // ---------------------------------------------------------------------------
 typedef void (*KernelFn)(const Args);
@@ -479,6 +668,17 @@ KernelFn pick_kind(int kind, bool bwd, bool vec, bool flat)
 }
 
 }  // namespace
+
+hipError_t launch_tiles(int dtype, int kind, bool backward, const TileArgs &args, uint32_t ntiles,
+                        hipStream_t stream)
+{
+    TileFn fn = dtype == F32 ? (backward ? pick_tile<SF32, true>(kind) : pick_tile<SF32, false>(kind))
+              : dtype == F16 ? (backward ? pick_tile<SF16, true>(kind) : pick_tile<SF16, false>(kind))
+                             : (backward ? pick_tile<SBf16, true>(kind) : pick_tile<SBf16, false>(kind));
+    TileArgs copy = args;
+    void *kargs[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(ntiles), dim3(256), kargs, 0, stream);
+}
 
 hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args, hipStream_t stream)
 {

@@ -17,6 +17,13 @@ torch.nn.Linear layers (hipBLASLt GEMMs on ROCm).
 In-place backward (the default, as in the profile above): the gradient
 overwrites the saved activation inputs, which therefore must not be used by
 anything else after the backward.  Pass inplace_backward=False to keep them.
+
+Operands in other layouts (transposed or sliced activations, broadcast
+incoming gradients such as the one of ``y.sum()``) go to the strided entry
+points without a copy ("Write a Triton SiLU-Mul (SwiGLU) Kernel", Common
+failure modes: thread the strides through instead of silently reading a
+transposed view); only views whose leading dimensions cannot be merged into
+one are copied to a contiguous tensor first.
 """
 from __future__ import annotations
 
@@ -28,19 +35,35 @@ from . import glu as _glu
 _KINDS = ("silu", "gelu_erf", "gelu_tanh", "relu")
 
 
-def _ready(t: torch.Tensor) -> torch.Tensor:
-    """Incoming gradients may be views the ABI cannot take (broadcast rows
-    with stride 0, transposed or unmergeable views); make those contiguous
-    (this allocates)."""
+def _row_major(t: torch.Tensor) -> bool:
+    """True when glu_fwd / glu_bwd take t as it is: last dimension contiguous
+    and leading dimensions merging into rows at least a row apart."""
     if t.dim() == 0 or (t.shape[-1] > 1 and t.stride(-1) != 1):
-        return t.contiguous()
+        return False
     try:
         v = t.view(-1, t.shape[-1])
     except RuntimeError:
+        return False
+    return v.shape[0] <= 1 or v.stride(0) >= v.shape[1]
+
+
+def _writable(t: torch.Tensor) -> bool:
+    """t can take a result in place: it merges into 2-D and no two of its
+    elements share memory (no stride 0 along a dimension of size > 1)."""
+    return _viewable(t) is t and all(st != 0 for n, st in zip(t.shape, t.stride()) if n > 1)
+
+
+def _viewable(t: torch.Tensor) -> torch.Tensor:
+    """t itself when its leading dimensions merge into one (any strides: the
+    strided entry points take transposed, sliced and broadcast views), else a
+    contiguous copy (this allocates)."""
+    if t.dim() == 0:
+        return t   # rejected by the binding: the activation needs a dimension
+    try:
+        t.view(-1, t.shape[-1])
+        return t
+    except RuntimeError:
         return t.contiguous()
-    if v.shape[0] > 1 and v.stride(0) < v.shape[1]:
-        return t.contiguous()
-    return t
 
 
 class GatedActivation(torch.autograd.Function):
@@ -48,7 +71,10 @@ class GatedActivation(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, a, b, kind: str, inplace_backward: bool):
-        y = _glu.glu_fwd(kind, "separate", a, b)
+        if _row_major(a) and _row_major(b):
+            y = _glu.glu_fwd(kind, "separate", a, b)
+        else:
+            y = _glu.glu_fwd_strided(kind, _viewable(a), _viewable(b))
         ctx.save_for_backward(a, b)
         ctx.kind = kind
         ctx.inplace_backward = inplace_backward
@@ -57,11 +83,18 @@ class GatedActivation(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dy):
         a, b = ctx.saved_tensors
-        dy = _ready(dy)
-        if ctx.inplace_backward:
-            _glu.glu_bwd(ctx.kind, "separate", a, b, dy, inplace=True)
+        inplace = ctx.inplace_backward
+        if _row_major(a) and _row_major(b) and _row_major(dy):
+            if inplace:
+                _glu.glu_bwd(ctx.kind, "separate", a, b, dy, inplace=True)
+                return a, b, None, None
+            da, db = _glu.glu_bwd(ctx.kind, "separate", a, b, dy, inplace=False)
+            return da, db, None, None
+        dy = _viewable(dy)
+        if inplace and _writable(a) and _writable(b):
+            _glu.glu_bwd_strided(ctx.kind, a, b, dy, da=a, db=b)
             return a, b, None, None
-        da, db = _glu.glu_bwd(ctx.kind, "separate", a, b, dy, inplace=False)
+        da, db = _glu.glu_bwd_strided(ctx.kind, _viewable(a), _viewable(b), dy)
         return da, db, None, None
 
 
@@ -70,7 +103,14 @@ class FusedGatedActivation(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, kind: str, inplace_backward: bool):
-        y = _glu.glu_fwd(kind, "gate_up", x)
+        if _row_major(x):
+            y = _glu.glu_fwd(kind, "gate_up", x)
+        else:
+            if x.shape[-1] % 2:
+                raise ValueError(f"gate_up input width {x.shape[-1]} is odd")
+            xv = _viewable(x)
+            i = x.shape[-1] // 2
+            y = _glu.glu_fwd_strided(kind, xv[..., :i], xv[..., i:])
         ctx.save_for_backward(x)
         ctx.kind = kind
         ctx.inplace_backward = inplace_backward
@@ -79,11 +119,21 @@ class FusedGatedActivation(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dy):
         (x,) = ctx.saved_tensors
-        dy = _ready(dy)
-        if ctx.inplace_backward:
-            _glu.glu_bwd(ctx.kind, "gate_up", x, None, dy, inplace=True)
+        inplace = ctx.inplace_backward
+        if _row_major(x) and _row_major(dy):
+            if inplace:
+                _glu.glu_bwd(ctx.kind, "gate_up", x, None, dy, inplace=True)
+                return x, None, None
+            dx = _glu.glu_bwd(ctx.kind, "gate_up", x, None, dy, inplace=False)
+            return dx, None, None
+        dy = _viewable(dy)
+        i = x.shape[-1] // 2
+        if inplace and _writable(x):
+            _glu.glu_bwd_strided(ctx.kind, x[..., :i], x[..., i:], dy, da=x[..., :i], db=x[..., i:])
             return x, None, None
-        dx = _glu.glu_bwd(ctx.kind, "gate_up", x, None, dy, inplace=False)
+        xv = _viewable(x)
+        dx = torch.empty_like(xv)
+        _glu.glu_bwd_strided(ctx.kind, xv[..., :i], xv[..., i:], dy, da=dx[..., :i], db=dx[..., i:])
         return dx, None, None
 
 

@@ -6,10 +6,13 @@ the result is computed by the library's gfx950 kernels.  PyTorch supplies the
 device memory and the stream.  Importing this module loads the library and
 raises ImportError if it has not been built (there is no fallback).
 
-Tensors: the activation dimension is the last one and must be contiguous
-(column stride 1); leading dimensions are merged into rows, which must be
-possible without a copy ("Write a Triton SiLU-Mul (SwiGLU) Kernel",
-"Common failure modes": never silently read a transposed view).
+Tensors: for ``glu_fwd`` / ``glu_bwd`` the activation dimension is the last
+one and must be contiguous (column stride 1); leading dimensions are merged
+into rows, which must be possible without a copy ("Write a Triton SiLU-Mul
+(SwiGLU) Kernel", "Common failure modes": never silently read a transposed
+view).  ``glu_fwd_strided`` / ``glu_bwd_strided`` take any views whose
+leading dimensions merge into one (transposed, sliced, broadcast) and pass
+both strides to the library.
 """
 from __future__ import annotations
 
@@ -34,6 +37,10 @@ _lib.glu_bwd.restype = _i
 _lib.glu_add_rmsnorm_fwd.argtypes = [_i, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p,
                                      ctypes.c_float, _p]
 _lib.glu_add_rmsnorm_fwd.restype = _i
+_lib.glu_fwd_strided.argtypes = [_i, _i, _i64, _i64] + [_p, _i64, _i64] * 3 + [_p]
+_lib.glu_fwd_strided.restype = _i
+_lib.glu_bwd_strided.argtypes = [_i, _i, _i64, _i64] + [_p, _i64, _i64] * 5 + [_p]
+_lib.glu_bwd_strided.restype = _i
 _lib.glu_status_string.argtypes = [_i]
 _lib.glu_status_string.restype = ctypes.c_char_p
 _lib.glu_version.argtypes = []
@@ -77,7 +84,8 @@ def _rows(t: torch.Tensor, name: str) -> torch.Tensor:
     if t.dim() == 0:
         raise ValueError(f"{name} must have at least one dimension")
     if t.shape[-1] > 1 and t.stride(-1) != 1:
-        raise ValueError(f"{name}: the last dimension must be contiguous (stride 1), got {t.stride()}")
+        raise ValueError(f"{name}: the last dimension must be contiguous (stride 1), got {t.stride()}; "
+                         "glu_fwd_strided / glu_bwd_strided take other layouts")
     try:
         return t.view(-1, t.shape[-1]) if t.dim() != 2 else t
     except RuntimeError as e:
@@ -268,3 +276,71 @@ def glu_add_rmsnorm_fwd(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Te
     if st != 0:
         raise GluError(st, "glu_add_rmsnorm_fwd")
     return h, y, rstd
+
+
+def _view2(t: torch.Tensor, name: str):
+    """(rows, cols, row stride, column stride) of t seen as a 2-D matrix over
+    its last dimension, without copying."""
+    if t.dim() == 0:
+        raise ValueError(f"{name} must have at least one dimension")
+    if t.dim() == 1:
+        return 1, t.shape[0], t.shape[0], t.stride(0)
+    try:
+        v = t.view(-1, t.shape[-1])
+    except RuntimeError as e:
+        raise ValueError(f"{name}: leading dimensions cannot be merged without a copy") from e
+    return v.shape[0], v.shape[1], v.stride(0), v.stride(1)
+
+
+def _strided_operands(named, shape, dtype, device):
+    out = []
+    for name, t in named:
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        _, _, rs, cs = _view2(t, name)
+        out += [_ptr(t), rs, cs]
+    return out
+
+
+def glu_fwd_strided(kind: str, a: torch.Tensor, b: torch.Tensor, y: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """y = act(a) * b for views a, b, y of one shape and any strides.  y is
+    allocated with a's layout when None; y may be a or b itself (in place)."""
+    k = _code(KINDS, kind, "kind")
+    dt = _code(DTYPES, a.dtype, "dtype")
+    if a.device.type != "cuda":
+        raise ValueError("tensors must be on a ROCm (cuda) device")
+    if y is None:
+        y = torch.empty_like(a)
+    rows, cols, _, _ = _view2(a, "a")
+    ops = _strided_operands([("a", a), ("b", b), ("y", y)], a.shape, a.dtype, a.device)
+    with torch.cuda.device(a.device):
+        st = _lib.glu_fwd_strided(k, dt, rows, cols, *ops, _stream(a.device, stream))
+    if st != 0:
+        raise GluError(st, "glu_fwd_strided")
+    return y
+
+
+def glu_bwd_strided(kind: str, a: torch.Tensor, b: torch.Tensor, dy: torch.Tensor,
+                    da: torch.Tensor | None = None, db: torch.Tensor | None = None, stream=None):
+    """da = dy * act'(a) * b, db = dy * act(a) for views of one shape and any
+    strides.  da, db are allocated with a's layout when None; pass da=a,
+    db=b to write the gradients over the inputs.  Returns (da, db)."""
+    k = _code(KINDS, kind, "kind")
+    dt = _code(DTYPES, a.dtype, "dtype")
+    if a.device.type != "cuda":
+        raise ValueError("tensors must be on a ROCm (cuda) device")
+    da = torch.empty_like(a) if da is None else da
+    db = torch.empty_like(a) if db is None else db
+    rows, cols, _, _ = _view2(a, "a")
+    ops = _strided_operands([("a", a), ("b", b), ("dy", dy), ("da", da), ("db", db)], a.shape, a.dtype,
+                            a.device)
+    with torch.cuda.device(a.device):
+        st = _lib.glu_bwd_strided(k, dt, rows, cols, *ops, _stream(a.device, stream))
+    if st != 0:
+        raise GluError(st, "glu_bwd_strided")
+    return da, db

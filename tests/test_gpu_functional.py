@@ -83,7 +83,7 @@ def test_leaf_inputs_out_of_place(fn):
 
 
 def test_expanded_incoming_gradient(fn):
-    """A broadcast (stride-0) incoming gradient is made contiguous first."""
+    """A broadcast (stride-0) incoming gradient goes to the strided kernels as is."""
     g = torch.Generator().manual_seed(43)
     a0 = (torch.randn(16, 256, generator=g) * 2).to(torch.bfloat16).cuda().requires_grad_()
     b0 = torch.randn(16, 256, generator=g).to(torch.bfloat16).cuda().requires_grad_()
