@@ -41,6 +41,7 @@ KERNEL_SOURCES = ["mlp_gated_activation_amd/csrc/glu_kernels.hip",
                   "mlp_gated_activation_amd/csrc/glu_taylor.h",
                   "mlp_gated_activation_amd/csrc/glu_erfc.h"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_glu_swiglu_bf16_4096x14336.md")
+TILE_PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_glu_tile_swiglu_bf16_4096x14336_dyT.md")
 RMS_SOURCES = ["mlp_gated_activation_amd/csrc/rmsnorm_kernels.hip", "mlp_gated_activation_amd/csrc/rmsnorm_internal.h"]
 RMS_PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_add_rmsnorm_bf16_4096x{h}.md")
 
@@ -98,6 +99,29 @@ def cpu_baseline(a, b, dy):
         "elements_per_s": round(N / best, 1),
         "seconds_per_step": round(best, 4),
     }
+
+
+def copy_reference(torch, dev, stream):
+    """GB/s of torch's plain device copy (one read + one write) of 3/2 of a
+    bf16 (4096, 14336) operand pair; also the reference kernel the HBM
+    counters are calibrated on."""
+    src = torch.empty(2 * N * ES * 3 // 2, dtype=torch.uint8, device=dev)
+    dsts = [torch.empty_like(src) for _ in range(3)]
+    for d in dsts:
+        d.copy_(src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    reps = 30
+    for r in range(reps):
+        dsts[r % 3].copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() / (c0.elapsed_time(c1) / reps * 1e-3) / 1e9
+    del src, dsts
+    torch.cuda.empty_cache()
+    return round(copy_gbs, 1)
 
 
 def main():
@@ -216,24 +240,7 @@ def main():
                  "note": "F.silu(a) * b and autograd, bf16, same buffers; algorithmic bytes / time"}
 
     # attainable reference: a plain device copy (1 read + 1 write) of the same bytes
-    copy = None
-    if args.copy_check:
-        src = torch.empty(2 * N * ES * 3 // 2, dtype=torch.uint8, device=dev)
-        dsts = [torch.empty_like(src) for _ in range(3)]
-        for d in dsts:
-            d.copy_(src)
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        c0.record(stream)
-        reps = 30
-        for r in range(reps):
-            dsts[r % 3].copy_(src)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        copy_gbs = 2 * src.numel() / (c0.elapsed_time(c1) / reps * 1e-3) / 1e9
-        copy = round(copy_gbs, 1)
-        del src, dsts
+    copy = copy_reference(torch, dev, stream) if args.copy_check else None
 
     achieved = BWD_BYTES / (bwd_avg * 1e-3) / 1e9
     traffic = committed_traffic()
@@ -427,7 +434,11 @@ def bench_strided(args, torch, glu, inputs, dev):
         glu.glu_bwd_strided("silu", aT, bT, dyT, da=aT, db=bT)
 
     t_allT = timed(all_T, args.steps)
+    del tsets, sets
+    torch.cuda.empty_cache()
+    copy = copy_reference(torch, dev, stream) if args.copy_check else None
     gbs = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 1)
+    traffic = committed_traffic(TILE_PMC_SUMMARY, "bwd_traffic_bytes")
     value = gbs(BWD_BYTES, t_bwd)
     result = {
         "metric": "achieved HBM GB/s (% of peak) for bf16 silu backward, transposed dy view, 4096x14336",
@@ -447,9 +458,10 @@ def bench_strided(args, torch, glu, inputs, dev):
             "copy_then_bwd": {"avg_us": round(1e3 * t_copy, 2), "GBps": gbs(BWD_BYTES, t_copy),
                               "path": "dy.contiguous() + row-major backward"},
         },
+        "torch_copy_GBps": copy,
         "roofline": {"bound": "hbm", "kernel": "glu_tile_kernel<bf16, silu, bwd>", "achieved": value,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4),
-                     "traffic": None},
+                     "traffic": traffic},
         "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)

@@ -379,6 +379,15 @@ glu_status strided(bool bwd, int kind, int dtype, int64_t rows, int64_t cols, co
         t.out[i] = reinterpret_cast<void *>(outs[i].p);
         t.out_mode[i] = mode(outs[i], &t.ors[i], &t.ocs[i]);
     }
+    // LDS slots: transposed inputs first; outputs reuse them after the math
+    int nti = 0, nto = 0;
+    for (int i = 0; i < nin; ++i)
+        if (t.in_mode[i] == glu::kTransposed)
+            t.in_slot[i] = uint8_t(nti++);
+    for (int i = 0; i < nout; ++i)
+        if (t.out_mode[i] == glu::kTransposed)
+            t.out_slot[i] = uint8_t(nto++);
+    t.nslots = uint8_t(nti > nto ? nti : nto);
     t.rows = R;
     t.cols = C;
     t.tiles_r = uint32_t(tr);

@@ -109,6 +109,9 @@ struct TileArgs {
     uint32_t tile0;         // first tile (in launch order) of this launch
     uint8_t in_mode[3];     // TileMode per operand
     uint8_t out_mode[2];
+    uint8_t in_slot[3];     // LDS slot of each kTransposed operand
+    uint8_t out_slot[2];
+    uint8_t nslots;         // slots the launch allocates: max(transposed inputs, transposed outputs)
 };
 
 #ifndef GLU_TILE_GROUP

@@ -501,7 +501,9 @@ __global__ void __launch_bounds__(256) glu_tile_kernel(const TileArgs p)
     constexpr int VE = T::VE;                             // elements per 16-byte chunk
     constexpr int LINE = kTile / VE;                      // chunks per tile line
     constexpr int CPT = kTile * kTile / (256 * VE);       // chunks per thread
-    __shared__ float lds[NIN][kTile][kTile + 1];
+    // nslots slots of kTile x (kTile + 1) floats, sized at launch
+    extern __shared__ float lds_raw[];
+    float(*lds)[kTile][kTile + 1] = reinterpret_cast<float(*)[kTile][kTile + 1]>(lds_raw);
 
     const TileCoord tc = tile_coord(p.tile0 + blockIdx.x, p.tiles_r, p.tiles_c);
     const int64_t r0 = int64_t(tc.r) * kTile, c0 = int64_t(tc.c) * kTile;
@@ -556,7 +558,7 @@ __global__ void __launch_bounds__(256) glu_tile_kernel(const TileArgs p)
                 const int q = tid + 256 * j, line = q / LINE, seg = q % LINE;
 #pragma unroll
                 for (int e = 0; e < VE; ++e)
-                    lds[k][seg * VE + e][line] = x[k][j][e];
+                    lds[p.in_slot[k]][seg * VE + e][line] = x[k][j][e];
             }
         }
     __syncthreads();
@@ -568,7 +570,7 @@ __global__ void __launch_bounds__(256) glu_tile_kernel(const TileArgs p)
                 const int q = tid + 256 * j, line = q / LINE, seg = q % LINE;
 #pragma unroll
                 for (int e = 0; e < VE; ++e)
-                    x[k][j][e] = lds[k][line][seg * VE + e];
+                    x[k][j][e] = lds[p.in_slot[k]][line][seg * VE + e];
             }
         }
 
@@ -601,7 +603,7 @@ __global__ void __launch_bounds__(256) glu_tile_kernel(const TileArgs p)
                 const int q = tid + 256 * j, line = q / LINE, seg = q % LINE;
 #pragma unroll
                 for (int e = 0; e < VE; ++e)
-                    lds[k][line][seg * VE + e] = y[k][j][e];
+                    lds[p.out_slot[k]][line][seg * VE + e] = y[k][j][e];
             }
         }
     __syncthreads();
@@ -613,9 +615,15 @@ __global__ void __launch_bounds__(256) glu_tile_kernel(const TileArgs p)
         for (int j = 0; j < CPT; ++j) {
             const int q = tid + 256 * j, line = q / LINE, seg = q % LINE;
             float v[VE];
+            if (tr) {
 #pragma unroll
-            for (int e = 0; e < VE; ++e)
-                v[e] = tr ? lds[k][seg * VE + e][line] : y[k][j][e];
+                for (int e = 0; e < VE; ++e)
+                    v[e] = lds[p.out_slot[k]][seg * VE + e][line];
+            } else {
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    v[e] = y[k][j][e];
+            }
             const int64_t r = tr ? r0 + seg * VE : r0 + line, c = tr ? c0 + line : c0 + seg * VE;
             const bool full = mode != kGather && (tr ? (c < p.cols && r + VE <= p.rows) : (r < p.rows && c + VE <= p.cols));
             if (full) {
@@ -677,7 +685,8 @@ hipError_t launch_tiles(int dtype, int kind, bool backward, const TileArgs &args
                              : (backward ? pick_tile<SBf16, true>(kind) : pick_tile<SBf16, false>(kind));
     TileArgs copy = args;
     void *kargs[] = {&copy};
-    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(ntiles), dim3(256), kargs, 0, stream);
+    const size_t lds = size_t(args.nslots) * kTile * (kTile + 1) * sizeof(float);
+    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(ntiles), dim3(256), kargs, lds, stream);
 }
 
 hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args, hipStream_t stream)

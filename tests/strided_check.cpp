@@ -143,6 +143,28 @@ int main(int argc, char **argv)
         }
         if (next != tr * tc)
             return fail("tile coverage", next, tr * tc);
+        {
+            // LDS slots: distinct per transposed input, distinct per
+            // transposed output, all below nslots, nslots no larger than needed
+            const glu::TileArgs &t = glu::g_tiles[0].first;
+            int nti = 0, nto = 0, used_i = 0, used_o = 0;
+            for (int i = 0; i < nin; ++i)
+                if (t.in_mode[i] == glu::kTransposed) {
+                    ++nti;
+                    if (t.in_slot[i] >= t.nslots || (used_i >> t.in_slot[i]) & 1)
+                        return fail("input slot", i, t.in_slot[i]);
+                    used_i |= 1 << t.in_slot[i];
+                }
+            for (int i = 0; i < nout; ++i)
+                if (t.out_mode[i] == glu::kTransposed) {
+                    ++nto;
+                    if (t.out_slot[i] >= t.nslots || (used_o >> t.out_slot[i]) & 1)
+                        return fail("output slot", i, t.out_slot[i]);
+                    used_o |= 1 << t.out_slot[i];
+                }
+            if (t.nslots != (nti > nto ? nti : nto))
+                return fail("slot count", t.nslots);
+        }
         if (tr * tc <= (1ll << 24)) {
             // the launch order visits every tile exactly once
             std::vector<unsigned char> seen(size_t(tr * tc), 0);
