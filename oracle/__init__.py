@@ -16,6 +16,8 @@ applies the ``[gate | up]`` layout, which is pure slicing:
   backward writes ``da, db`` over the saved ``a, b``; in the fused layout the
   gradient is therefore ``dx = [da | db]``.
 * "Write a Triton Fused Add+RMSNorm Kernel": ``add_rmsnorm`` below.
+* "Fused Kernels", section 4: ``gemm_glu`` below, the gate and up
+  projections with the activation applied to their results.
 
 All inputs are the exact values of the stored (already rounded) tensors,
 given as float64 arrays; all outputs are unrounded float64.
@@ -69,6 +71,8 @@ def _load():
         lib.oracle_bwd.restype = None
         lib.oracle_add_rmsnorm.argtypes = [i64, i64, pd, pd, pd, d, pd, pd, pd]
         lib.oracle_add_rmsnorm.restype = None
+        lib.oracle_gemm_glu.argtypes = [ctypes.c_int, i64, i64, i64, pd, pd, pd, pd, pd, pd]
+        lib.oracle_gemm_glu.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -184,3 +188,24 @@ def add_rmsnorm(x, res, gamma, eps: float):
     _load().oracle_add_rmsnorm(rows, H, _ptr(x), _ptr(res), _ptr(gamma), float(eps),
                                _ptr(h), _ptr(y), _ptr(rstd))
     return h, y, rstd
+
+
+def gemm_glu(kind, x, wg, wu, want_gu: bool = False):
+    """h = act(x @ wg^T) * (x @ wu^T) ("Fused Kernels", section 4).
+
+    x: (M, K); wg, wu: (N, K), the [out][in] layout of a linear layer's
+    weight.  Returns h (M, N), or (h, g, u) with the pre-activations
+    g = x @ wg^T and u = x @ wu^T when want_gu.  fp64 sums in k order.
+    """
+    x, wg, wu = _f64(x), _f64(wg), _f64(wu)
+    if x.ndim != 2 or wg.ndim != 2 or wg.shape != wu.shape or wg.shape[1] != x.shape[1]:
+        raise ValueError("x must be (M, K) and wg, wu (N, K)")
+    M, K = x.shape
+    N = wg.shape[0]
+    h = np.empty((M, N))
+    g = np.empty((M, N)) if want_gu else None
+    u = np.empty((M, N)) if want_gu else None
+    null = ctypes.POINTER(ctypes.c_double)()
+    _load().oracle_gemm_glu(_kind(kind), M, N, K, _ptr(x), _ptr(wg), _ptr(wu), _ptr(h),
+                            _ptr(g) if want_gu else null, _ptr(u) if want_gu else null)
+    return (h, g, u) if want_gu else h

@@ -18,6 +18,7 @@
  *  [LIGER]   "Kernel Profile: SwiGLU (Tier 1 -- Element-wise)" (Liger-Kernel)
  *  [FUSED]   "Fused Kernels" (lesson 5)
  *  [RMSNORM] "Write a Triton Fused Add+RMSNorm Kernel"
+ *  [FUSED]   "Fused Kernels" (lesson 5), section 4 (the fused MLP)
  *
  * Readings where the pages leave a step open (all pinned by tests):
  *  - GELU-erf is evaluated as 0.5*x*erfc(-x/sqrt2), which equals the pages'
@@ -201,6 +202,39 @@ void oracle_add_rmsnorm(int64_t rows, int64_t H, const double *x, const double *
             yi[j] = hi[j] * rs * gamma[j];
         if (rstd)
             rstd[i] = rs;
+    }
+}
+
+/* Gate/up projection with the gated activation fused into it ([FUSED]
+ * section 4: gate and up tiles are accumulated, then silu(g) * u is applied
+ * in registers; [SWIGLU] "Do not use this when" and "Performance
+ * requirements": the activation fused into the matmul epilogue):
+ *   g[m][n] = sum_k x[m][k] * wg[n][k]
+ *   u[m][n] = sum_k x[m][k] * wu[n][k]
+ *   h[m][n] = act(g[m][n]) * u[m][n]
+ * x is M x K, wg and wu are N x K (the [out][in] layout of a linear layer's
+ * weight), all dense row-major.  The sums run over k in order in fp64
+ * (products of 16-bit inputs are exact in fp64); nothing is rounded to a
+ * storage type.  g and u may be NULL. */
+void oracle_gemm_glu(int kind, int64_t M, int64_t N, int64_t K, const double *x, const double *wg,
+                     const double *wu, double *h, double *g, double *u)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        const double *xm = x + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const double *gn = wg + n * K, *un = wu + n * K;
+            double sg = 0.0, su = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                sg += xm[k] * gn[k];
+                su += xm[k] * un[k];
+            }
+            h[m * N + n] = oracle_act(kind, sg) * su;
+            if (g)
+                g[m * N + n] = sg;
+            if (u)
+                u[m * N + n] = su;
+        }
     }
 }
 
