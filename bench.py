@@ -37,6 +37,7 @@ FWD_BYTES = 3 * N * ES          # read a, b; write y
 BWD_BYTES = 5 * N * ES          # read a, b, dy; write da, db
 STEP_BYTES = FWD_BYTES + BWD_BYTES
 KERNEL_SOURCES = ["mlp_gated_activation_amd/csrc/glu_kernels.hip",
+                  "mlp_gated_activation_amd/csrc/glu_act.h",
                   "mlp_gated_activation_amd/csrc/glu_internal.h",
                   "mlp_gated_activation_amd/csrc/glu_taylor.h",
                   "mlp_gated_activation_amd/csrc/glu_erfc.h"]
@@ -127,10 +128,12 @@ def copy_reference(torch, dev, stream):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=["glu", "add_rmsnorm", "glu_strided"], default="glu",
+    ap.add_argument("--op", choices=["glu", "add_rmsnorm", "glu_strided", "gemm_glu"], default="glu",
                     help="glu: the SwiGLU fwd+bwd step (default); add_rmsnorm: the fused residual "
                          "add + RMSNorm forward, bf16, 4096 rows; glu_strided: the SwiGLU backward "
-                         "with a transposed incoming gradient (LDS-tiled kernel) and related layouts")
+                         "with a transposed incoming gradient (LDS-tiled kernel) and related layouts; "
+                         "gemm_glu: the gate/up projection with the activation fused into its epilogue "
+                         "(bf16, 4096 tokens, hidden 4096, I 14336)")
     ap.add_argument("--hidden", type=int, default=4096, help="add_rmsnorm only: row width")
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
@@ -164,6 +167,8 @@ def main():
         return bench_add_rmsnorm(args, torch, glu, inputs, dev)
     if args.op == "glu_strided":
         return bench_strided(args, torch, glu, inputs, dev)
+    if args.op == "gemm_glu":
+        return bench_gemm(args, torch, glu, inputs, dev)
     w = inputs.WORKLOADS["swiglu_bf16_4096x14336"]
     a_h, b_h, dy_h = w.make(seed=0)
     sets = []
@@ -464,6 +469,103 @@ def bench_strided(args, torch, glu, inputs, dev):
                      "traffic": traffic},
         "cpu_baseline": None,
     }
+    print(json.dumps(result), flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def bench_gemm(args, torch, glu, inputs, dev):
+    """Gate/up projection with the activation fused into the GEMM epilogue
+    ("Fused Kernels", section 4), bf16 SwiGLU: x (4096, 4096), fused
+    [gate | up] weight (2*14336, 4096), h (4096, 14336).  Flops per step:
+    2 * M * K * 2N.  Compared with hipBLASLt (F.linear) producing [g | u]
+    followed by this library's elementwise forward."""
+    M, K, N = 4096, 4096, 14336
+    flops = 2 * M * K * 2 * N
+    x_h, w_h = inputs.gemm_glu(M, N, K, "bf16", seed=0)
+    nsets = 2
+    sets = [(x_h.to(dev), w_h.to(dev), torch.empty(M, N, dtype=torch.bfloat16, device=dev)) for _ in range(nsets)]
+    gu = torch.empty(M, 2 * N, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    import torch.nn.functional as F
+    steps = min(args.steps, 200)
+
+    def timed(fn, n):
+        for i in range(min(n, 10)):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def fused(i):
+        x, w, h = sets[i % nsets]
+        glu.glu_gemm_fwd("silu", x, w, h=h)
+
+    def fused_gu(i):
+        x, w, h = sets[i % nsets]
+        glu.glu_gemm_fwd("silu", x, w, h=h, gu=gu)
+
+    def blas_only(i):
+        x, w, h = sets[i % nsets]
+        torch.matmul(x, w.t(), out=gu)
+
+    def blas_then_glu(i):
+        x, w, h = sets[i % nsets]
+        torch.matmul(x, w.t(), out=gu)
+        glu.glu_fwd("silu", "gate_up", gu, y=h)
+
+    t_fused = timed(fused, steps)
+    t_fused_gu = timed(fused_gu, steps)
+    t_blas = timed(blas_only, steps)
+    t_unfused = timed(blas_then_glu, steps)
+    tf = lambda ms: round(flops / (ms * 1e-3) / 1e12, 1)
+    value = tf(t_fused)
+    result = {
+        "metric": "achieved TFLOP/s (% of bf16 MFMA peak) for the gate/up projection with the SwiGLU "
+                  "activation fused into its epilogue, 4096 tokens x hidden 4096 -> I 14336",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": 10,
+        "ms_per_step": round(t_fused, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded x ~ N(0,1), w ~ N(0, 0.02^2), bf16; 2 rotating buffer sets)",
+        "config": {"workload": "h = silu(x @ Wg^T) * (x @ Wu^T), bf16, M=4096, K=4096, N=14336, fp32 accumulation",
+                   "M": M, "K": K, "N": N, "flops_per_step": flops},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels": {
+            "fused": {"avg_us": round(1e3 * t_fused, 1), "TFLOPs": value},
+            "fused_with_gu": {"avg_us": round(1e3 * t_fused_gu, 1), "TFLOPs": tf(t_fused_gu),
+                              "note": "also writes the pre-activations [g | u] for a backward"},
+            "hipblaslt_gemm_only": {"avg_us": round(1e3 * t_blas, 1), "TFLOPs": tf(t_blas),
+                                    "note": "torch.matmul x @ W^T -> [g | u], no activation"},
+            "hipblaslt_then_glu_fwd": {"avg_us": round(1e3 * t_unfused, 1), "TFLOPs": tf(t_unfused),
+                                       "note": "the unfused path: GEMM writes [g | u], glu_fwd reads it"},
+        },
+        "speedup_vs_unfused": round(t_unfused / t_fused, 3),
+        "roofline": {"bound": "mfma", "kernel": "gemm_glu_kernel<bf16, silu>", "achieved": value,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    del sets, gu
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = M
+        fx = x_h[:rows].to(torch.float64).numpy()
+        fw = w_h.to(torch.float64).numpy()
+        t0 = time.perf_counter()
+        oracle.gemm_glu("silu", fx, fw[:N], fw[N:])
+        dt = time.perf_counter() - t0
+        sample_flops = 2 * rows * K * 2 * N
+        result["cpu_baseline"] = {"value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "sample": "the full workload (fp64 scalar C, OpenMP over rows), one run",
+                                  "seconds": round(dt, 2)}
     print(json.dumps(result), flush=True)
 
 

@@ -169,6 +169,40 @@ GLU_API glu_status glu_bwd_strided(glu_kind kind, glu_dtype dtype, int64_t rows,
                            hipStream_t stream);
 
 /*
+ * Gate/up projection with the gated activation fused into its epilogue
+ * ("Fused Kernels", section 4: the gate and up tiles are accumulated and
+ * silu(g) * u is applied in registers; "Write a Triton SiLU-Mul (SwiGLU)
+ * Kernel", Do not use this when and Performance requirements: fusing the
+ * activation into the matmul epilogue saves the round trip of g and u
+ * through HBM):
+ *
+ *   g[m][n] = sum_k x[m][k] * w_gate[n][k],  u[m][n] = sum_k x[m][k] * w_up[n][k],
+ *   h[m][n] = act(g[m][n]) * u[m][n]
+ *
+ * x is M x K (row stride ldx), w_gate and w_up are N x K: the [out][in]
+ * layout of a linear layer's weight (for one fused [gate | up] weight of
+ * 2N rows, w_up = w_gate + N * ldw).  h is M x N (row stride ldh).  The
+ * products accumulate in fp32 on the matrix cores; act(g) * u is evaluated
+ * in fp32 and rounded once (RNE) to the storage type.
+ * gu (optional, NULL to skip): the pre-activations, rounded to the storage
+ * type, in the [gate | up] layout: g at gu[m][n], u at gu[m][N + n], row
+ * stride ldgu >= 2N.  That is the input glu_bwd takes with GLU_GATE_UP.
+ *
+ * dtype: GLU_BF16 or GLU_F16 (GLU_ERR_ENUM for GLU_F32).
+ * x, w_gate, w_up must be 16-byte aligned with K, ldx, ldwg, ldwu multiples
+ * of 8 elements; h and gu aligned to the element size (GLU_ERR_ARG
+ * otherwise).  ldx, ldwg, ldwu >= K and ldh >= N (GLU_ERR_STRIDE).  M, N,
+ * K < 2^31, ldx, ldwg, ldwu < 2^24 and at most 2^24 workgroup tiles of
+ * 256 x 128 (GLU_ERR_SHAPE).
+ * h and gu must not overlap the inputs or each other (GLU_ERR_ALIAS).
+ * M == 0 or N == 0 is a no-op; K == 0 gives h = 0.
+ */
+GLU_API glu_status glu_gemm_fwd(glu_kind kind, glu_dtype dtype, int64_t M, int64_t N, int64_t K,
+                        const void *x, int64_t ldx, const void *w_gate, int64_t ldwg,
+                        const void *w_up, int64_t ldwu, void *h, int64_t ldh,
+                        void *gu, int64_t ldgu, hipStream_t stream);
+
+/*
  * Fused residual add + RMSNorm forward, one row of `hidden` values at a time
  * ("Write a Triton Fused Add+RMSNorm Kernel", Required reasoning process,
  * steps 1-7, and Correctness requirements):

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libglu.so")
 SOURCES = [os.path.join(CSRC, "glu_kernels.hip"), os.path.join(CSRC, "rmsnorm_kernels.hip"),
-           os.path.join(CSRC, "glu_api.cpp")]
+           os.path.join(CSRC, "gemm_kernels.hip"), os.path.join(CSRC, "glu_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

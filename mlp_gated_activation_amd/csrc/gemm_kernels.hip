@@ -1,0 +1,377 @@
+// gemm_kernels.hip -- gfx950 MFMA kernel for the gate/up projection with the
+// gated activation fused into its epilogue:
+//   g = x @ wg^T,  u = x @ wu^T,  h = act(g) * u
+// ("Fused Kernels", section 4: gate and up tiles are accumulated and the
+// activation is applied in registers; "Write a Triton SiLU-Mul (SwiGLU)
+// Kernel", Do not use this when / Performance requirements: fusing the
+// activation into the matmul epilogue saves the round trip of g and u
+// through HBM).
+//
+// This is a dense contraction, so it runs on the matrix cores:
+//  - a workgroup of 256 threads (4 waves, 2 x 2) owns 256 rows of x and 128
+//    columns of h, i.e. 128 gate and 128 up rows of the weights; each wave
+//    holds a 128 x 64 block of g and the same block of u in 16 fp32
+//    accumulators of v_mfma_f32_32x32x16_{bf16,f16};
+//  - both operands are k-contiguous (x rows, weight rows), so every MFMA
+//    fragment is one 16-byte LDS read;
+//  - k advances 64 at a time through two LDS stages of 64 KiB; the next
+//    stage is fetched with direct global-to-LDS loads (no registers, no LDS
+//    write instructions) while the current stage's MFMAs run; stage rows are
+//    128 bytes with XOR-swizzled 16-byte chunks so fragment reads spread
+//    over the banks; the MFMA fragments of the next 16-deep k step are read
+//    while the current step's MFMAs issue;
+//  - g and u of one element sit in the same lane and register slot, so the
+//    epilogue act(g) * u is lane-local; h is rounded once to the storage type
+//    and leaves four features (8 bytes) per store.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "glu_act.h"
+#include "glu_internal.h"
+
+namespace glu {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename E> struct MfmaOp;
+template <> struct MfmaOp<__bf16> {
+    __device__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    }
+};
+template <> struct MfmaOp<_Float16> {
+    __device__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    }
+};
+
+constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
+constexpr int ROWS = BM + 2 * BN;               // x rows, then gate rows, then up rows
+constexpr int ROW_BYTES = BK * 2;               // one row of a stage
+constexpr int CPR = BK / 8;                     // 16-byte chunks per row
+constexpr int RPI = 1024 / ROW_BYTES;           // rows per wave load instruction (1 KiB)
+constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
+constexpr int NST = (128 * 1024) / STAGE_BYTES; // LDS stages (128 KiB in all)
+constexpr int PREF = NST - 1;                   // stages in flight ahead of the one computed
+constexpr int LOADS = 128 / RPI;                // load instructions per wave per stage
+constexpr int KSTEPS = BK / 16;                 // 16-deep MFMA steps per stage
+static_assert(NST >= 2 && NST <= 4, "two to four stages");
+
+// Chunk c of stage row r sits at position c ^ swz(r) of the row.  The 16
+// lanes one LDS cycle serves read 16 consecutive rows at one logical chunk;
+// rows 256 bytes apart share banks, so they get distinct positions.
+__device__ inline int swz(int r) { return (r / (256 / ROW_BYTES)) % CPR; }
+
+typedef __attribute__((address_space(3))) void lds_t;
+typedef const __attribute__((address_space(1))) void gbl_t;
+
+// Scheduling hints for the compiler's machine scheduler (instruction-class
+// masks of __builtin_amdgcn_sched_group_barrier).
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+
+#ifndef GLU_GEMM_DMA
+#define GLU_GEMM_DMA 1
+#endif
+
+// s_waitcnt immediates: wait until at most n of this wave's vector-memory
+// loads are outstanding (n < 64), LDS and export counters untouched.
+template <int n> constexpr int vm_wait() { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Workgroup barrier without a memory fence: the caller has already waited for
+// its own LDS writes (the counters above); the empty asm keeps the compiler
+// from moving memory accesses across it.
+__device__ inline void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <typename E, int KIND>
+__global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
+{
+    __shared__ u32x4 lds_v[NST * STAGE_BYTES / 16];
+    char *lds = reinterpret_cast<char *>(lds_v);
+
+    const uint32_t nt = p.tiles_m * p.tiles_n;
+    const TileCoord tc = grouped_coord(xcd_remap(blockIdx.x, nt), p.tiles_m, p.tiles_n, kGemmGroup);
+    const int64_t m0 = int64_t(tc.r) * BM, n0 = int64_t(tc.c) * BN;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+
+    // Loads: wave w fills stage rows [128 w, 128 w + 128): x rows for waves
+    // 0-1, gate rows for wave 2, up rows for wave 3.  Instruction j covers
+    // rows 128 w + RPI j + lane / CPR; lane puts logical chunk
+    // (lane % CPR) ^ swz(row) at position lane % CPR, i.e. at LDS byte
+    // row * ROW_BYTES + 16 * (lane % CPR): one contiguous KiB per wave
+    // instruction, the layout the direct-to-LDS load writes.  Rows past M or
+    // N are read from a valid row (clamped); their results are never stored.
+    // The wave index is uniform: keep everything the load addresses need in
+    // scalar registers, plus one 32-bit byte offset per lane and instruction
+    // from the tile's first row (row strides are below 2^24 elements, so the
+    // offsets fit).
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const char *gbase;
+    int64_t gld, gfirst, glimit;
+    if (wu < 2) {
+        gbase = static_cast<const char *>(p.x);
+        gld = p.ldx;
+        gfirst = m0 + 128 * wu;
+        glimit = p.M;
+    } else {
+        gbase = static_cast<const char *>(wu == 2 ? p.wg : p.wu);
+        gld = wu == 2 ? p.ldwg : p.ldwu;
+        gfirst = n0;
+        glimit = p.N;
+    }
+    const int64_t fc = gfirst < glimit ? gfirst : glimit - 1;
+    const char *tbase = gbase + fc * gld * 2;
+    const int lrow = lane / CPR, lpos = lane % CPR;
+    uint32_t goff[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int r = 128 * wu + RPI * j + lrow;
+        int64_t row = gfirst + RPI * j + lrow;
+        row = row < glimit ? row : glimit - 1;
+        goff[j] = uint32_t(((row - fc) * gld + 8 * (lpos ^ swz(r))) * 2);
+    }
+    auto issue_direct = [&](int buf, int k0, int j) {
+        __builtin_amdgcn_global_load_lds((gbl_t *)(tbase + int64_t(k0) * 2 + uint64_t(goff[j])),
+                                         (lds_t *)(lds + buf * STAGE_BYTES + (128 * wu + RPI * j) * ROW_BYTES), 16,
+                                         0, 0);
+    };
+    // The last stage may be partial: zero past K, through registers (the
+    // waits before the next barrier cover its LDS writes).
+    auto issue_partial = [&](int buf, int k0) {
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int r = 128 * wu + RPI * j + lrow;
+            const int kc = 8 * (lpos ^ swz(r));
+            const u32x4 v = k0 + kc < p.K ? *reinterpret_cast<const u32x4 *>(tbase + int64_t(k0) * 2 + uint64_t(goff[j]))
+                                          : u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4 *>(lds + buf * STAGE_BYTES + r * ROW_BYTES + 16 * lpos) = v;
+        }
+    };
+
+    f32x16 accg[4][2], accu[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            accg[i][j] = f32x16{0};
+            accu[i][j] = f32x16{0};
+        }
+
+    // Fragment reads: row r, logical chunk c -> LDS byte r*ROW_BYTES + 16*(c ^ swz(r)).
+    const int hi = lane >> 5;
+    const int ra = wm * 128 + (lane & 31), rg = BM + wn * 64 + (lane & 31), ru = BM + BN + wn * 64 + (lane & 31);
+    struct Frags {
+        u32x4 a[4], g[2], u[2];
+    };
+    auto read = [&](const char *st, int ks, Frags &f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = ra + 32 * i;
+            f.a[i] = *reinterpret_cast<const u32x4 *>(st + r * ROW_BYTES + 16 * ((2 * ks + hi) ^ swz(r)));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r1 = rg + 32 * j, r2 = ru + 32 * j;
+            f.g[j] = *reinterpret_cast<const u32x4 *>(st + r1 * ROW_BYTES + 16 * ((2 * ks + hi) ^ swz(r1)));
+            f.u[j] = *reinterpret_cast<const u32x4 *>(st + r2 * ROW_BYTES + 16 * ((2 * ks + hi) ^ swz(r2)));
+        }
+    };
+    auto mfmas = [&](const Frags &f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                accg[i][j] = MfmaOp<E>::run(f.g[j], f.a[i], accg[i][j]);
+                accu[i][j] = MfmaOp<E>::run(f.u[j], f.a[i], accu[i][j]);
+            }
+    };
+    // One stage: KSTEPS 16-deep steps.  The fragments of step ks + 1 are
+    // read while step ks's 16 MFMAs issue; with `direct`, the loads of a
+    // later stage go out during the first step (GLU_GEMM_DMA: straight into
+    // LDS; otherwise into registers, written to LDS during the last step).
+#if !GLU_GEMM_DMA
+    u32x4 stg[LOADS];
+#endif
+    auto stage = [&](const char *st, bool direct, int nbuf, int k1) {
+        Frags f[2];
+        read(st, 0, f[0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            if (ks == 0 && direct) {
+#pragma unroll
+                for (int j = 0; j < LOADS; ++j) {
+#if GLU_GEMM_DMA
+                    issue_direct(nbuf, k1, j);
+#else
+                    stg[j] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4 *>(tbase + int64_t(k1) * 2 + uint64_t(goff[j])));
+#endif
+                }
+            }
+#if !GLU_GEMM_DMA
+            if (ks + 1 == KSTEPS && direct) {
+#pragma unroll
+                for (int j = 0; j < LOADS; ++j)
+                    *reinterpret_cast<u32x4 *>(lds + nbuf * STAGE_BYTES + (128 * wu + RPI * j + lrow) * ROW_BYTES +
+                                               16 * lpos) = stg[j];
+            }
+#endif
+            if (ks + 1 < KSTEPS)
+                read(st, ks + 1, f[(ks + 1) & 1]);
+            mfmas(f[ks & 1]);
+            if (ks + 1 < KSTEPS) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                    if (ks == 0 && direct)
+                        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (LOADS + 7) / 8, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
+            } else {
+                if (ks == 0 && direct)
+                    for (int q = 0; q < LOADS; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+                    }
+#if !GLU_GEMM_DMA
+                if (direct)
+                    for (int q = 0; q < LOADS; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+                    }
+#endif
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
+            }
+            // nothing crosses between steps: each step's MFMAs use only
+            // fragments read one step earlier
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Wait until at most `ahead` later stages of this wave's loads are in
+    // flight, then barrier: the stage about to be computed is in LDS.
+    auto wait_stage = [&](int ahead) {
+        if (ahead >= 2)
+            __builtin_amdgcn_s_waitcnt(vm_wait<2 * LOADS>());
+        else if (ahead == 1)
+            __builtin_amdgcn_s_waitcnt(vm_wait<LOADS>());
+        else
+            __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_waitcnt(vm_wait<63>() & ~(15 << 8));   // LDS writes of the partial stage
+        lds_barrier();
+    };
+
+    const int KT = (p.K + BK - 1) / BK, KF = p.K / BK;   // stages, full stages
+    // Prologue: the first PREF stages.
+#pragma unroll
+    for (int s = 0; s < PREF; ++s) {
+        if (s < KF)
+            for (int j = 0; j < LOADS; ++j)
+                issue_direct(s, s * BK, j);
+        else if (s < KT)
+            issue_partial(s, s * BK);
+    }
+    int kt = 0;
+    // Main loop: the stage PREF ahead is a full one, fetched directly into LDS.
+    for (; kt + PREF < KF; ++kt) {
+        wait_stage(PREF - 1);
+        stage(lds + (kt % NST) * STAGE_BYTES, true, (kt + PREF) % NST, (kt + PREF) * BK);
+    }
+    // The remaining stages; the partial one (if any) goes through registers.
+    for (; kt < KT; ++kt) {
+        const int ahead = KT - 1 - kt < PREF - 1 ? KT - 1 - kt : PREF - 1;
+        wait_stage(ahead);
+        if (kt + PREF < KT)
+            issue_partial((kt + PREF) % NST, (kt + PREF) * BK);
+        stage(lds + (kt % NST) * STAGE_BYTES, false, 0, 0);
+    }
+    lds_barrier();
+
+    // Epilogue.  The MFMAs take the weight rows as their first operand, so
+    // each 32 x 32 block is g^T: lane holds token row m = lane % 32 of the
+    // block and, for e < 16, feature column 8*(e/4) + 4*(lane/32) + e%4.
+    // Four consecutive features of one token leave as one 8-byte store.
+    E *h = static_cast<E *>(p.h);
+    E *gu = static_cast<E *>(p.gu);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    auto put4 = [&](E *base, int64_t n, const float *v) {
+        // 4 values for columns n .. n+3 of one row (masked at N)
+        if (n + 3 < p.N && (reinterpret_cast<uintptr_t>(base + n) & 7) == 0) {
+            typedef E ex4 __attribute__((ext_vector_type(4)));
+            ex4 q;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                q[t] = static_cast<E>(v[t]);
+            *reinterpret_cast<u32x2 *>(base + n) = __builtin_bit_cast(u32x2, q);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (n + t < p.N)
+                    base[n + t] = static_cast<E>(v[t]);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + wm * 128 + i * 32 + (lane & 31);
+        if (m >= p.M)
+            continue;
+        E *hrow = h + m * p.ldh;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n0 + wn * 64 + j * 32 + q * 8 + (lane >> 5) * 4;
+                float hv[4], gv[4], uv[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    gv[t] = accg[i][j][4 * q + t];
+                    uv[t] = accu[i][j][4 * q + t];
+                    hv[t] = act<KIND, float>(gv[t]) * uv[t];
+                }
+                put4(hrow, n, hv);
+                if (gu) {
+                    put4(gu + m * p.ldgu, n, gv);
+                    put4(gu + m * p.ldgu + p.N, n, uv);
+                }
+            }
+    }
+}
+
+typedef void (*GemmFn)(const GemmArgs);
+
+template <typename E> GemmFn pick_gemm(int kind)
+{
+    switch (kind) {
+    case SILU: return &gemm_glu_kernel<E, SILU>;
+    case GELU_ERF: return &gemm_glu_kernel<E, GELU_ERF>;
+    case GELU_TANH: return &gemm_glu_kernel<E, GELU_TANH>;
+    default: return &gemm_glu_kernel<E, RELU>;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_glu(int dtype, int kind, const GemmArgs &args, hipStream_t stream)
+{
+    GemmFn fn = dtype == F16 ? pick_gemm<_Float16>(kind) : pick_gemm<__bf16>(kind);
+    GemmArgs copy = args;
+    void *kargs[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(args.tiles_m * args.tiles_n), dim3(256), kargs, 0,
+                           stream);
+}
+
+}  // namespace glu

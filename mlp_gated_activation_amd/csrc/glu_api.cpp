@@ -405,6 +405,75 @@ glu_status strided(bool bwd, int kind, int dtype, int64_t rows, int64_t cols, co
 
 extern "C" {
 
+glu_status glu_gemm_fwd(glu_kind kind, glu_dtype dtype, int64_t M, int64_t N, int64_t K, const void *x,
+                        int64_t ldx, const void *w_gate, int64_t ldwg, const void *w_up, int64_t ldwu, void *h,
+                        int64_t ldh, void *gu, int64_t ldgu, hipStream_t stream)
+{
+    if (!(kind >= GLU_SILU && kind <= GLU_RELU) || !(dtype == GLU_F16 || dtype == GLU_BF16))
+        return GLU_ERR_ENUM;
+    if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return GLU_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return GLU_OK;
+    if (h == nullptr)
+        return GLU_ERR_NULL;
+    if (K == 0) {
+        // h = act(0) * 0: the inputs are never read
+        x = w_gate = w_up = nullptr;
+        ldx = ldwg = ldwu = 0;
+    } else if (x == nullptr || w_gate == nullptr || w_up == nullptr) {
+        return GLU_ERR_NULL;
+    }
+    int64_t two_n = 2 * N;
+    if (ldx < K || ldwg < K || ldwu < K || ldh < N || (gu != nullptr && ldgu < two_n))
+        return GLU_ERR_STRIDE;
+    const int es = 2;
+    const uintptr_t px = uintptr_t(x), pg = uintptr_t(w_gate), pu = uintptr_t(w_up), ph = uintptr_t(h),
+                    pgu = uintptr_t(gu);
+    if (!aligned16(px) || !aligned16(pg) || !aligned16(pu) || (K & 7) || (ldx & 7) || (ldwg & 7) || (ldwu & 7) ||
+        (ph & 1) || (pgu & 1))
+        return GLU_ERR_ARG;
+    const int64_t in_rows = K == 0 ? 0 : 1;   // inputs take no bytes when K == 0
+    const int64_t tm = (M + glu::kGemmBM - 1) / glu::kGemmBM, tn = (N + glu::kGemmBN - 1) / glu::kGemmBN;
+    if (tm * tn > int64_t(glu::kMaxGemmTiles) || ldx >= glu::kGemmMaxLd || ldwg >= glu::kGemmMaxLd ||
+        ldwu >= glu::kGemmMaxLd)
+        return GLU_ERR_SHAPE;
+    // byte extents of every operand (overflow -> shape error)
+    const Region rx{px, ldx, K}, rg{pg, ldwg, K}, ru{pu, ldwu, K}, rh{ph, ldh, N}, rgu{pgu, ldgu, two_n};
+    int64_t ex, eg, eu, eh, egu = 0;
+    if (!extent_bytes(M, rx, es, &ex) || !extent_bytes(N, rg, es, &eg) || !extent_bytes(N, ru, es, &eu) ||
+        !extent_bytes(M, rh, es, &eh) || (gu != nullptr && !extent_bytes(M, rgu, es, &egu)))
+        return GLU_ERR_SHAPE;
+    ex *= in_rows;
+    eg *= in_rows;
+    eu *= in_rows;
+    auto apart = [](uintptr_t a, int64_t ea, uintptr_t b, int64_t eb) {
+        return a + uintptr_t(ea) <= b || b + uintptr_t(eb) <= a;
+    };
+    if (!apart(ph, eh, px, ex) || !apart(ph, eh, pg, eg) || !apart(ph, eh, pu, eu))
+        return GLU_ERR_ALIAS;
+    if (gu != nullptr && (!apart(pgu, egu, px, ex) || !apart(pgu, egu, pg, eg) || !apart(pgu, egu, pu, eu) ||
+                          overlaps(M, rh, Region{pgu, ldgu, two_n}, es)))
+        return GLU_ERR_ALIAS;
+    glu::GemmArgs a{};
+    a.x = x;
+    a.wg = w_gate;
+    a.wu = w_up;
+    a.h = h;
+    a.gu = gu;
+    a.ldx = ldx;
+    a.ldwg = ldwg;
+    a.ldwu = ldwu;
+    a.ldh = ldh;
+    a.ldgu = ldgu;
+    a.M = int32_t(M);
+    a.N = int32_t(N);
+    a.K = int32_t(K);
+    a.tiles_m = uint32_t(tm);
+    a.tiles_n = uint32_t(tn);
+    return glu::launch_gemm_glu(dtype, kind, a, stream) == hipSuccess ? GLU_OK : GLU_ERR_HIP;
+}
+
 glu_status glu_fwd_strided(glu_kind kind, glu_dtype dtype, int64_t rows, int64_t cols, const void *a, int64_t a_rs,
                            int64_t a_cs, const void *b, int64_t b_rs, int64_t b_cs, void *y, int64_t y_rs,
                            int64_t y_cs, hipStream_t stream)

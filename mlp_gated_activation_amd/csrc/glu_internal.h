@@ -134,14 +134,29 @@ constexpr uint32_t kTileGroup = GLU_TILE_GROUP;
 struct TileCoord {
     uint32_t r, c;
 };
-GLU_HD inline TileCoord tile_coord(uint32_t t, uint32_t tiles_r, uint32_t tiles_c)
+GLU_HD inline TileCoord grouped_coord(uint32_t t, uint32_t tiles_r, uint32_t tiles_c, uint32_t group)
 {
-    const uint64_t per_group = uint64_t(kTileGroup) * tiles_c;
+    const uint64_t per_group = uint64_t(group) * tiles_c;
     const uint32_t g = uint32_t(t / per_group);
-    const uint32_t first = g * kTileGroup;
-    const uint32_t h = tiles_r - first < kTileGroup ? tiles_r - first : kTileGroup;
+    const uint32_t first = g * group;
+    const uint32_t h = tiles_r - first < group ? tiles_r - first : group;
     const uint64_t in_g = t - uint64_t(g) * per_group;
     return TileCoord{first + uint32_t(in_g % h), uint32_t(in_g / h)};
+}
+GLU_HD inline TileCoord tile_coord(uint32_t t, uint32_t tiles_r, uint32_t tiles_c)
+{
+    return grouped_coord(t, tiles_r, tiles_c, kTileGroup);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  xcd_remap gives XCD x a contiguous range of the launch order, so the
+// workgroups that run together on one XCD work on neighbouring tiles.  It is
+// a bijection on [0, n) for any n.
+constexpr uint32_t kXcds = 8;
+GLU_HD inline uint32_t xcd_remap(uint32_t b, uint32_t n)
+{
+    const uint32_t q = n / kXcds, r = n % kXcds, x = b % kXcds;
+    return x * q + (x < r ? x : r) + b / kXcds;
 }
 
 // Largest tile count one launch covers.
@@ -150,6 +165,36 @@ constexpr uint32_t kMaxTilesPerLaunch = 1u << 22;
 
 hipError_t launch_tiles(int dtype, int kind, bool backward, const TileArgs &args, uint32_t ntiles,
                         hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Gate/up projection with the activation in the epilogue (gemm_kernels.hip).
+// Workgroup tile: kGemmBM rows of x by kGemmBN columns of h, i.e. kGemmBN
+// gate rows and kGemmBN up rows of the weights, kGemmBK deep per stage.
+// ---------------------------------------------------------------------------
+#ifndef GLU_GEMM_BK
+#define GLU_GEMM_BK 64
+#endif
+constexpr int kGemmBM = 256, kGemmBN = 128, kGemmBK = GLU_GEMM_BK;
+#ifndef GLU_GEMM_GROUP
+#define GLU_GEMM_GROUP 4
+#endif
+constexpr uint32_t kGemmGroup = GLU_GEMM_GROUP;   // row tiles per group of the launch order
+
+struct GemmArgs {
+    const void *x, *wg, *wu;  // x: M x K, wg / wu: N x K ([out][in]), 16-byte aligned rows
+    void *h;                  // M x N
+    void *gu;                 // optional: g at gu[m][n], u at gu[m][N + n] (or NULL)
+    int64_t ldx, ldwg, ldwu, ldh, ldgu;
+    int32_t M, N, K;
+    uint32_t tiles_m, tiles_n;
+};
+// Largest workgroup count of one GEMM launch (grid * 256 below 2^32).
+constexpr uint32_t kMaxGemmTiles = 1u << 24;
+// Input row strides stay below this (elements): a workgroup addresses its
+// 128 rows of an operand with 32-bit byte offsets.
+constexpr int64_t kGemmMaxLd = int64_t(1) << 24;
+
+hipError_t launch_gemm_glu(int dtype, int kind, const GemmArgs &args, hipStream_t stream);
 
 // Enqueues one launch; returns the HIP status of hipLaunchKernel.
 hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args,

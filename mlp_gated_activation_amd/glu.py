@@ -41,6 +41,8 @@ _lib.glu_fwd_strided.argtypes = [_i, _i, _i64, _i64] + [_p, _i64, _i64] * 3 + [_
 _lib.glu_fwd_strided.restype = _i
 _lib.glu_bwd_strided.argtypes = [_i, _i, _i64, _i64] + [_p, _i64, _i64] * 5 + [_p]
 _lib.glu_bwd_strided.restype = _i
+_lib.glu_gemm_fwd.argtypes = [_i, _i, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+_lib.glu_gemm_fwd.restype = _i
 _lib.glu_status_string.argtypes = [_i]
 _lib.glu_status_string.restype = ctypes.c_char_p
 _lib.glu_version.argtypes = []
@@ -344,3 +346,54 @@ def glu_bwd_strided(kind: str, a: torch.Tensor, b: torch.Tensor, dy: torch.Tenso
     if st != 0:
         raise GluError(st, "glu_bwd_strided")
     return da, db
+
+
+def glu_gemm_fwd(kind: str, x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor | None = None,
+                 h: torch.Tensor | None = None, gu=False, stream=None):
+    """h = act(x @ w_gate^T) * (x @ w_up^T) on the matrix cores, with the
+    activation in the GEMM epilogue ("Fused Kernels", section 4).
+
+    x: (..., K); w_gate, w_up: (N, K), the weights of two linear layers; with
+    w_up None, w_gate is one fused (2N, K) [gate | up] weight.  h (allocated
+    if None) has shape (..., N).  gu=True also returns the pre-activations in
+    the [gate | up] layout (..., 2N) (a tensor may be passed instead), which
+    glu_bwd(kind, "gate_up", ...) takes.  Returns h, or (h, gu).
+    bf16 / fp16 only; K and the row strides must be multiples of 8.
+    """
+    k = _code(KINDS, kind, "kind")
+    dt = _code(DTYPES, x.dtype, "dtype")
+    if x.device.type != "cuda":
+        raise ValueError("tensors must be on a ROCm (cuda) device")
+    if w_up is None:
+        if w_gate.dim() != 2 or w_gate.shape[0] % 2:
+            raise ValueError("a fused [gate | up] weight must be (2N, K)")
+        n = w_gate.shape[0] // 2
+        w_gate, w_up = w_gate[:n], w_gate[n:]
+    if w_gate.dim() != 2 or w_up.shape != w_gate.shape or w_gate.shape[1] != x.shape[-1]:
+        raise ValueError(f"weights must be (N, K) with K = x.shape[-1]; got {tuple(w_gate.shape)}, "
+                         f"{tuple(w_up.shape)} for x {tuple(x.shape)}")
+    N, K = w_gate.shape
+    x2 = _rows(x, "x")
+    wg2, wu2 = _rows(w_gate, "w_gate"), _rows(w_up, "w_up")
+    out_shape = x.shape[:-1] + (N,)
+    if h is None:
+        h = torch.empty(out_shape, dtype=x.dtype, device=x.device)
+    if tuple(h.shape) != tuple(out_shape):
+        raise ValueError(f"h has shape {tuple(h.shape)}, expected {tuple(out_shape)}")
+    h2 = _rows(h, "h")
+    if gu is True:
+        gu = torch.empty(x.shape[:-1] + (2 * N,), dtype=x.dtype, device=x.device)
+    elif gu is False or gu is None:
+        gu = None
+    if gu is not None and tuple(gu.shape) != tuple(x.shape[:-1] + (2 * N,)):
+        raise ValueError(f"gu has shape {tuple(gu.shape)}, expected {tuple(x.shape[:-1] + (2 * N,))}")
+    gu2 = _rows(gu, "gu") if gu is not None else None
+    _check([("w_gate", w_gate), ("w_up", w_up), ("h", h), ("gu", gu)], x.dtype, x.device)
+    M = x2.shape[0]
+    with torch.cuda.device(x.device):
+        st = _lib.glu_gemm_fwd(k, dt, M, N, K, _ptr(x2), _ld(x2), _ptr(wg2), _ld(wg2), _ptr(wu2), _ld(wu2),
+                               _ptr(h2), _ld(h2), _ptr(gu2), _ld(gu2) if gu2 is not None else 0,
+                               _stream(x.device, stream))
+    if st != 0:
+        raise GluError(st, "glu_gemm_fwd")
+    return (h, gu) if gu is not None else h

@@ -93,6 +93,19 @@ def add_rmsnorm(rows: int, hidden: int, dtype: str, seed: int = 0):
     return x, res, gamma
 
 
+def gemm_glu(M: int, N: int, K: int, dtype: str, w_std: float = 0.02, seed: int = 0):
+    """x (M, K) and a fused [gate | up] weight w (2N, K) for the gate/up
+    projection with the fused activation ("Fused Kernels", section 4).
+    Draw order: ``x = randn(M, K)``, ``w = w_std * randn(2N, K)`` (the usual
+    0.02 initialisation of a linear layer, so g and u are about N(0, K*w_std^2)).
+    """
+    g = _gen(seed)
+    t = DTYPES[dtype]
+    x = torch.randn(M, K, generator=g).to(t)
+    w = (torch.randn(2 * N, K, generator=g) * w_std).to(t)
+    return x, w
+
+
 def all_bit_patterns(dtype: str) -> torch.Tensor:
     """Every 16-bit pattern of a 16-bit dtype, in bit order, as a 1-D tensor."""
     t = DTYPES[dtype]

@@ -34,8 +34,8 @@ def declared_functions():
 
 def test_header_declarations_are_exported():
     names = declared_functions()
-    assert set(names) == {"glu_fwd", "glu_bwd", "glu_fwd_strided", "glu_bwd_strided", "glu_add_rmsnorm_fwd",
-                          "glu_status_string", "glu_version"}
+    assert set(names) == {"glu_fwd", "glu_bwd", "glu_fwd_strided", "glu_bwd_strided", "glu_gemm_fwd",
+                          "glu_add_rmsnorm_fwd", "glu_status_string", "glu_version"}
     nm = subprocess.run(["nm", "-D", "--defined-only", glu.library_path()],
                         capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in nm.splitlines() if " T " in l}
@@ -149,6 +149,33 @@ def test_bwd_strided_rejects(args, want):
     assert sbwd(**args) == want
 
 
+def gemm(kind=0, dtype=BF16, M=4, N=16, K=64, x=P, ldx=64, wg=P + (1 << 20), ldwg=64, wu=P + (2 << 20),
+         ldwu=64, h=P + (3 << 20), ldh=16, gu=None, ldgu=0):
+    return lib.glu_gemm_fwd(kind, dtype, M, N, K, x, ldx, wg, ldwg, wu, ldwu, h, ldh, gu, ldgu, None)
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(kind=4), ENUM), (dict(dtype=F32), ENUM), (dict(dtype=3), ENUM),
+    (dict(M=-1), SHAPE), (dict(N=-1), SHAPE), (dict(K=-8), SHAPE), (dict(M=1 << 31), SHAPE),
+    (dict(M=0, x=None, wg=None, wu=None, h=None), OK), (dict(N=0, h=None), OK),
+    (dict(h=None), NULL), (dict(x=None), NULL), (dict(wg=None), NULL), (dict(wu=None), NULL),
+    (dict(ldx=56), STRIDE), (dict(ldwg=8), STRIDE), (dict(ldh=15), STRIDE),
+    (dict(gu=P + (4 << 20), ldgu=31), STRIDE),
+    (dict(K=60, ldx=64), ARG),                              # K not a multiple of 8
+    (dict(ldx=68), ARG), (dict(ldwu=72 + 4), ARG),          # row strides not 16-byte multiples
+    (dict(x=P + 8), ARG), (dict(wg=P + (1 << 20) + 2), ARG),
+    (dict(h=P + (3 << 20) + 1), ARG),
+    (dict(M=1 << 20, N=1 << 20, ldh=1 << 20), SHAPE),      # more than 2^24 workgroup tiles
+    (dict(h=P + 64), ALIAS),                                # h inside x
+    (dict(h=P + (2 << 20) - 16), ALIAS),                    # h runs into w_up
+    (dict(gu=P + (1 << 20), ldgu=32), ALIAS),               # gu over w_gate
+    (dict(gu=P + (3 << 20) + 8, ldgu=32), ALIAS),           # gu over h
+])
+def test_gemm_rejects(args, want):
+    # rejected or empty calls only: an accepted call would launch a kernel
+    assert gemm(**args) == want
+
+
 def rms(dtype=BF16, rows=4, hidden=64, x=P, ldx=64, r=P + (1 << 20), ldr=64, g=P + (2 << 20),
         h=P + (3 << 20), ldh=64, y=P + (4 << 20), ldy=64, rstd=P + (5 << 20), eps=1e-6):
     return lib.glu_add_rmsnorm_fwd(dtype, rows, hidden, x, ldx, r, ldr, g, h, ldh, y, ldy, rstd, eps, None)
@@ -211,6 +238,39 @@ int main() {
     assert out.stdout.strip() == "0"
 
 
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_gemm_tile_order_is_a_bijection():
+    """xcd_remap followed by grouped_coord (the GEMM's workgroup -> tile map)
+    visits every (row tile, column tile) exactly once, for grids that do and
+    do not divide by the 8 XCDs or the group height."""
+    src = r"""
+#include "glu_internal.h"
+#include <cstdio>
+#include <vector>
+int main() {
+    int bad = 0;
+    const unsigned shapes[][2] = {{16, 112}, {1, 1}, {1, 7}, {3, 5}, {5, 3}, {17, 9}, {33, 113}, {4, 8}, {7, 1},
+                                  {2, 1000}, {1000, 2}, {13, 13}};
+    for (auto &sh : shapes) {
+        const unsigned tm = sh[0], tn = sh[1], n = tm * tn;
+        std::vector<int> seen(n, 0);
+        for (unsigned b = 0; b < n; ++b) {
+            const unsigned l = glu::xcd_remap(b, n);
+            if (l >= n) { ++bad; continue; }
+            const glu::TileCoord c = glu::grouped_coord(l, tm, tn, glu::kGemmGroup);
+            if (c.r >= tm || c.c >= tn) { ++bad; continue; }
+            seen[c.r * tn + c.c]++;
+        }
+        for (int v : seen) bad += v != 1;
+    }
+    std::printf("%d\n", bad);
+}
+"""
+    with tempfile.TemporaryDirectory() as tmp:
+        out = subprocess.run([_compile_host(src, tmp)], capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "0"
+
+
 @pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="needs hipcc")
 def test_kernel_isa():
     """The compiled gfx950 kernels: no MFMA and no packed fp32 ops anywhere,
@@ -268,6 +328,32 @@ def test_tile_kernel_isa():
             lds = int(re.search(r"\.group_segment_fixed_size:\s+(\d+)", block).group(1))
             scratch = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", block).group(1))
             assert lds == 0 and scratch == 0, block[:200]
+
+
+@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="needs hipcc")
+def test_gemm_kernel_isa():
+    """The gate/up GEMM kernels: 8 instances (bf16/fp16 x 4 kinds), MFMA in
+    the k loop, no scratch, no packed fp32, LDS within the 160 KiB of a CU."""
+    from mlp_gated_activation_amd import build as b
+    src = [s for s in b.SOURCES if s.endswith("gemm_kernels.hip")][0]
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [b.HIPCC, *[f for f in b.FLAGS if f not in ("-shared",)], f"-I{b.INCLUDE}", f"-I{b.CSRC}",
+               "--save-temps", "-c", src, "-o", os.path.join(tmp, "k.o")]
+        subprocess.run(cmd, cwd=tmp, check=True, capture_output=True)
+        asm = open(os.path.join(tmp, "gemm_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")).read()
+    names = re.findall(r"^(_Z\w*gemm_glu_kernel\w*):", asm, re.M)
+    assert len(names) == 8
+    for name in names:
+        pos = asm.find(name + ":")
+        body = asm[pos:asm.find("s_endpgm", pos)]
+        assert re.search(r"v_mfma_f32_32x32x16_(bf16|f16)", body), name
+        assert not re.search(r"v_pk_(add|mul|fma)_f32", body), name
+    meta = asm[asm.find("amdhsa.kernels"):]
+    for block in re.split(r"\n  - ", meta):
+        if "gemm_glu_kernel" in block:
+            lds = int(re.search(r"\.group_segment_fixed_size:\s+(\d+)", block).group(1))
+            scratch = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", block).group(1))
+            assert 0 < lds <= 160 * 1024 and scratch == 0, block[:200]
 
 
 @pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="needs hipcc")

@@ -1,0 +1,134 @@
+"""GPU parity of the gate/up projection with the fused activation
+(glu_gemm_fwd, through the C ABI) against the fp64 oracle, with the error
+bound derived in gemm_bounds.py ("Fused Kernels", section 4)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_bounds import h_bound, pre_bound
+from oracle.compare import FORMATS, ulp
+from mlp_gated_activation_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ("silu", "gelu_erf", "gelu_tanh", "relu")
+FMT = {torch.bfloat16: "bf16", torch.float16: "fp16"}
+
+
+@pytest.fixture(scope="module")
+def glu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from conftest import ensure_built
+    ensure_built()
+    from mlp_gated_activation_amd import glu as g
+    return g
+
+
+def f64(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def check_h(h, x, wg, wu, kind, what, min_one_ulp=0.99):
+    """h within the derived bound of the oracle everywhere, and within one
+    output ulp for at least `min_one_ulp` of the elements."""
+    fx, fg, fu = f64(x), f64(wg), f64(wu)
+    ref, g, u = oracle.gemm_glu(kind, fx, fg, fu, want_gu=True)
+    act_g = oracle.act(kind, g)
+    fmt = FMT[h.dtype]
+    got = f64(h)
+    err = np.abs(got - ref)
+    bound = h_bound(fmt, fx.shape[1], fx, fg, fu, ref, g, u, act_g)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside the bound; first at "
+                           f"{np.argwhere(bad)[0]}: got {got[bad][0]!r} want {ref[bad][0]!r} bound {bound[bad][0]!r}")
+    one = float(np.mean(err <= ulp(ref, FORMATS[fmt])))
+    assert one >= min_one_ulp, f"{what}: only {one:.4f} of the results within one output ulp"
+    return ref, g, u, one
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("kind", KINDS)
+def test_ragged_tiles(glu, kind, dtype):
+    """M, N, K spanning several workgroup tiles and k stages, all ragged."""
+    M, N, K = 300, 200, 136
+    x, w = inputs.gemm_glu(M, N, K, "bf16" if dtype == torch.bfloat16 else "fp16", w_std=0.1, seed=3)
+    gx, gw = x.cuda(), w.cuda()
+    h, gu = glu.glu_gemm_fwd(kind, gx, gw, gu=True)
+    torch.cuda.synchronize()
+    ref, g, u, _ = check_h(h, x, w[:N], w[N:], kind, f"{kind} {dtype}")
+    fmt = FMT[dtype]
+    for name, got, want, wt in (("g", gu[:, :N], g, w[:N]), ("u", gu[:, N:], u, w[N:])):
+        err = np.abs(f64(got) - want)
+        assert (err <= pre_bound(fmt, K, f64(x), f64(wt), want)).all(), f"{kind} pre-activation {name}"
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 8), (1, 129, 64), (257, 1, 8), (5, 7, 4104), (512, 256, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_edge_shapes(glu, shape):
+    M, N, K = shape
+    x, w = inputs.gemm_glu(M, N, K, "bf16", w_std=0.05, seed=5)
+    h = glu.glu_gemm_fwd("silu", x.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    check_h(h, x, w[:N], w[N:], "silu", f"shape {shape}", min_one_ulp=0.95)
+
+
+def test_separate_weights_strided_rows_and_canaries(glu):
+    """Separate gate and up weights with padded row strides, x a row slice
+    of a wider matrix, h written into a wider sentinel-filled buffer."""
+    g = torch.Generator().manual_seed(9)
+    M, N, K = 130, 150, 96
+    xb = torch.randn(M, K + 24, generator=g).to(torch.bfloat16)
+    wgb = (torch.randn(N, K + 8, generator=g) * 0.1).to(torch.bfloat16)
+    wub = (torch.randn(N, K + 16, generator=g) * 0.1).to(torch.bfloat16)
+    x, wg, wu = xb[:, 8:8 + K], wgb[:, :K], wub[:, 16:16 + K]
+    hb = torch.full((M, N + 5), 7.0, dtype=torch.bfloat16, device="cuda")
+    h = hb[:, 2:2 + N]
+    glu.glu_gemm_fwd("gelu_tanh", x.cuda(), wg.cuda(), wu.cuda(), h=h)
+    torch.cuda.synchronize()
+    check_h(h, x, wg, wu, "gelu_tanh", "strided")
+    assert bool((hb[:, :2] == 7.0).all() and (hb[:, 2 + N:] == 7.0).all()), "wrote outside h"
+
+
+def test_k_zero_and_empty(glu):
+    x = torch.zeros(4, 0, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(6, 0, dtype=torch.bfloat16, device="cuda")
+    h = torch.full((4, 3), 5.0, dtype=torch.bfloat16, device="cuda")
+    glu.glu_gemm_fwd("silu", x, w, h=h)
+    assert bool((h == 0).all())
+    e = glu.glu_gemm_fwd("silu", torch.zeros(0, 8, dtype=torch.bfloat16, device="cuda"),
+                         torch.zeros(6, 8, dtype=torch.bfloat16, device="cuda"))
+    assert e.shape == (0, 3)
+
+
+def test_full_size_sampled(glu):
+    """The MLP shape of the benchmark (4096 tokens, hidden 4096, I = 14336),
+    bf16, checked on 64 sampled rows x 256 sampled columns of h and gu."""
+    M, N, K = 4096, 14336, 4096
+    x, w = inputs.gemm_glu(M, N, K, "bf16", seed=0)
+    gx, gw = x.cuda(), w.cuda()
+    h, gu = glu.glu_gemm_fwd("silu", gx, gw, gu=True)
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(1)
+    rows = torch.randperm(M, generator=gen)[:64]
+    cols = torch.randperm(N, generator=gen)[:256]
+    rr, cc = rows.cuda(), cols.cuda()
+    hs = h[rr][:, cc]
+    ref, g, u, one = check_h(hs, x[rows], w[:N][cols], w[N:][cols], "silu", "full size")
+    for name, got, want, wt in (("g", gu[rr][:, cc], g, w[:N][cols]), ("u", gu[rr][:, cc + N], u, w[N:][cols])):
+        err = np.abs(f64(got) - want)
+        assert (err <= pre_bound("bf16", K, f64(x[rows]), f64(wt), want)).all(), f"full-size {name}"
+
+
+def test_rejects(glu):
+    x = torch.zeros(8, 16, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(32, 16, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(glu.GluError, match="GLU_ERR_ENUM"):
+        glu.glu_gemm_fwd("silu", x.float(), w.float())
+    with pytest.raises(glu.GluError, match="GLU_ERR_ARG"):
+        glu.glu_gemm_fwd("silu", x[:, :12], w[:, :12])          # K not a multiple of 8
+    with pytest.raises(glu.GluError, match="GLU_ERR_ALIAS"):
+        glu.glu_gemm_fwd("silu", x, w, h=w[:8, :16])           # h over the weights
