@@ -43,6 +43,12 @@ KERNEL_SOURCES = ["mlp_gated_activation_amd/csrc/glu_kernels.hip",
                   "mlp_gated_activation_amd/csrc/glu_erfc.h"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_glu_swiglu_bf16_4096x14336.md")
 TILE_PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_glu_tile_swiglu_bf16_4096x14336_dyT.md")
+GEMM_SOURCES = ["mlp_gated_activation_amd/csrc/gemm_kernels.hip",
+                "mlp_gated_activation_amd/csrc/glu_act.h",
+                "mlp_gated_activation_amd/csrc/glu_internal.h",
+                "mlp_gated_activation_amd/csrc/glu_taylor.h",
+                "mlp_gated_activation_amd/csrc/glu_erfc.h"]
+GEMM_PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_gemm_glu_swiglu_bf16_4096x4096x14336.md")
 RMS_SOURCES = ["mlp_gated_activation_amd/csrc/rmsnorm_kernels.hip", "mlp_gated_activation_amd/csrc/rmsnorm_internal.h"]
 RMS_PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_add_rmsnorm_bf16_4096x{h}.md")
 
@@ -525,6 +531,9 @@ def bench_gemm(args, torch, glu, inputs, dev):
     t_fused_gu = timed(fused_gu, steps)
     t_blas = timed(blas_only, steps)
     t_unfused = timed(blas_then_glu, steps)
+    del sets, gu
+    torch.cuda.empty_cache()
+    copy = copy_reference(torch, dev, stream) if args.copy_check else None
     tf = lambda ms: round(flops / (ms * 1e-3) / 1e12, 1)
     value = tf(t_fused)
     result = {
@@ -547,12 +556,12 @@ def bench_gemm(args, torch, glu, inputs, dev):
                                        "note": "the unfused path: GEMM writes [g | u], glu_fwd reads it"},
         },
         "speedup_vs_unfused": round(t_unfused / t_fused, 3),
+        "torch_copy_GBps": copy,
         "roofline": {"bound": "mfma", "kernel": "gemm_glu_kernel<bf16, silu>", "achieved": value,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": committed_traffic(GEMM_PMC_SUMMARY, "traffic_bytes", GEMM_SOURCES)},
         "cpu_baseline": None,
     }
-    del sets, gu
     if not args.no_cpu_baseline:
         import oracle
         rows = M

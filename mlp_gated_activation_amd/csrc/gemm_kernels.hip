@@ -75,11 +75,7 @@ typedef const __attribute__((address_space(1))) void gbl_t;
 
 // Scheduling hints for the compiler's machine scheduler (instruction-class
 // masks of __builtin_amdgcn_sched_group_barrier).
-constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
-
-#ifndef GLU_GEMM_DMA
-#define GLU_GEMM_DMA 1
-#endif
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 
 // s_waitcnt immediates: wait until at most n of this wave's vector-memory
 // loads are outstanding (n < 64), LDS and export counters untouched.
@@ -200,11 +196,7 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
     };
     // One stage: KSTEPS 16-deep steps.  The fragments of step ks + 1 are
     // read while step ks's 16 MFMAs issue; with `direct`, the loads of a
-    // later stage go out during the first step (GLU_GEMM_DMA: straight into
-    // LDS; otherwise into registers, written to LDS during the last step).
-#if !GLU_GEMM_DMA
-    u32x4 stg[LOADS];
-#endif
+    // later stage go straight into LDS during the first step.
     auto stage = [&](const char *st, bool direct, int nbuf, int k1) {
         Frags f[2];
         read(st, 0, f[0]);
@@ -213,23 +205,9 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
         for (int ks = 0; ks < KSTEPS; ++ks) {
             if (ks == 0 && direct) {
 #pragma unroll
-                for (int j = 0; j < LOADS; ++j) {
-#if GLU_GEMM_DMA
-                    issue_direct(nbuf, k1, j);
-#else
-                    stg[j] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4 *>(tbase + int64_t(k1) * 2 + uint64_t(goff[j])));
-#endif
-                }
-            }
-#if !GLU_GEMM_DMA
-            if (ks + 1 == KSTEPS && direct) {
-#pragma unroll
                 for (int j = 0; j < LOADS; ++j)
-                    *reinterpret_cast<u32x4 *>(lds + nbuf * STAGE_BYTES + (128 * wu + RPI * j + lrow) * ROW_BYTES +
-                                               16 * lpos) = stg[j];
+                    issue_direct(nbuf, k1, j);
             }
-#endif
             if (ks + 1 < KSTEPS)
                 read(st, ks + 1, f[(ks + 1) & 1]);
             mfmas(f[ks & 1]);
@@ -248,13 +226,6 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
                         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                         __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
                     }
-#if !GLU_GEMM_DMA
-                if (direct)
-                    for (int q = 0; q < LOADS; ++q) {
-                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
-                    }
-#endif
                 __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
             }
             // nothing crosses between steps: each step's MFMAs use only
