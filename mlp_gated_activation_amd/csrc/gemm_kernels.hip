@@ -37,16 +37,23 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// v_mfma_f32_32x32x16: 32 x 32 blocks, 16 deep, 16 accumulator registers.
+// (A 16 x 16 x 32 variant of this tiling needs twice the fragment registers
+// and spills.)
+constexpr int MF = 32, KD = 16;
+typedef f32x16 AccT;
+constexpr int ACC_E = MF * MF / 64;   // accumulator registers per lane
+
 template <typename E> struct MfmaOp;
 template <> struct MfmaOp<__bf16> {
-    __device__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c)
+    __device__ static AccT run(u32x4 a, u32x4 b, AccT c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                        c, 0, 0, 0);
     }
 };
 template <> struct MfmaOp<_Float16> {
-    __device__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c)
+    __device__ static AccT run(u32x4 a, u32x4 b, AccT c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                       0, 0, 0);
@@ -62,7 +69,11 @@ constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
 constexpr int NST = (128 * 1024) / STAGE_BYTES; // LDS stages (128 KiB in all)
 constexpr int PREF = NST - 1;                   // stages in flight ahead of the one computed
 constexpr int LOADS = 128 / RPI;                // load instructions per wave per stage
-constexpr int KSTEPS = BK / 16;                 // 16-deep MFMA steps per stage
+constexpr int KSTEPS = BK / KD;                 // MFMA k steps per stage
+constexpr int FX = 128 / MF;                    // x (token) fragments per wave
+constexpr int FW = 64 / MF;                     // gate (and up) fragments per wave
+constexpr int NREAD = FX + 2 * FW;              // fragment reads per k step
+constexpr int NMFMA = FX * 2 * FW;              // MFMAs per k step
 static_assert(NST >= 2 && NST <= 4, "two to four stages");
 
 // Chunk c of stage row r sits at position c ^ swz(r) of the row.  The 16
@@ -157,39 +168,41 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
         }
     };
 
-    f32x16 accg[4][2], accu[4][2];
+    AccT accg[FX][FW], accu[FX][FW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FX; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            accg[i][j] = f32x16{0};
-            accu[i][j] = f32x16{0};
+        for (int j = 0; j < FW; ++j) {
+            accg[i][j] = AccT{0};
+            accu[i][j] = AccT{0};
         }
 
-    // Fragment reads: row r, logical chunk c -> LDS byte r*ROW_BYTES + 16*(c ^ swz(r)).
-    const int hi = lane >> 5;
-    const int ra = wm * 128 + (lane & 31), rg = BM + wn * 64 + (lane & 31), ru = BM + BN + wn * 64 + (lane & 31);
+    // Fragment reads: lane reads row (lane % MF) of each fragment at logical
+    // chunk KD/8 * ks + lane / MF; row r, chunk c -> LDS byte
+    // r*ROW_BYTES + 16*(c ^ swz(r)).
+    const int kq = lane / MF;
+    const int ra = wm * 128 + (lane % MF), rg = BM + wn * 64 + (lane % MF), ru = BM + BN + wn * 64 + (lane % MF);
     struct Frags {
-        u32x4 a[4], g[2], u[2];
+        u32x4 a[FX], g[FW], u[FW];
+    };
+    auto frag = [&](const char *st, int r, int ks) -> u32x4 {
+        return *reinterpret_cast<const u32x4 *>(st + r * ROW_BYTES + 16 * (((KD / 8) * ks + kq) ^ swz(r)));
     };
     auto read = [&](const char *st, int ks, Frags &f) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = ra + 32 * i;
-            f.a[i] = *reinterpret_cast<const u32x4 *>(st + r * ROW_BYTES + 16 * ((2 * ks + hi) ^ swz(r)));
-        }
+        for (int i = 0; i < FX; ++i)
+            f.a[i] = frag(st, ra + MF * i, ks);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r1 = rg + 32 * j, r2 = ru + 32 * j;
-            f.g[j] = *reinterpret_cast<const u32x4 *>(st + r1 * ROW_BYTES + 16 * ((2 * ks + hi) ^ swz(r1)));
-            f.u[j] = *reinterpret_cast<const u32x4 *>(st + r2 * ROW_BYTES + 16 * ((2 * ks + hi) ^ swz(r2)));
+        for (int j = 0; j < FW; ++j) {
+            f.g[j] = frag(st, rg + MF * j, ks);
+            f.u[j] = frag(st, ru + MF * j, ks);
         }
     };
     auto mfmas = [&](const Frags &f) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FX; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < FW; ++j) {
                 accg[i][j] = MfmaOp<E>::run(f.g[j], f.a[i], accg[i][j]);
                 accu[i][j] = MfmaOp<E>::run(f.u[j], f.a[i], accu[i][j]);
             }
@@ -213,20 +226,20 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
             mfmas(f[ks & 1]);
             if (ks + 1 < KSTEPS) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
+                for (int q = 0; q < NREAD; ++q) {
                     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
                     if (ks == 0 && direct)
-                        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (LOADS + 7) / 8, 0);
+                        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (LOADS + NREAD - 1) / NREAD, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NREAD, 0);
             } else {
                 if (ks == 0 && direct)
                     for (int q = 0; q < LOADS; ++q) {
                         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                         __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
                     }
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA, 0);
             }
             // nothing crosses between steps: each step's MFMAs use only
             // fragments read one step earlier
@@ -296,16 +309,17 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
         }
     };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wm * 128 + i * 32 + (lane & 31);
+    for (int i = 0; i < FX; ++i) {
+        const int64_t m = m0 + wm * 128 + i * MF + (lane % MF);
         if (m >= p.M)
             continue;
         E *hrow = h + m * p.ldh;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FW; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + wn * 64 + j * 32 + q * 8 + (lane >> 5) * 4;
+            for (int q = 0; q < ACC_E / 4; ++q) {
+                // features of registers 4q .. 4q+3: 8q + 4*(lane/32) + t
+                const int64_t n = n0 + wn * 64 + j * MF + q * 8 + (lane >> 5) * 4;
                 float hv[4], gv[4], uv[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {

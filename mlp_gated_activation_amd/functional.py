@@ -137,6 +137,51 @@ class FusedGatedActivation(torch.autograd.Function):
         return dx, None, None
 
 
+class FusedGateUpActivation(torch.autograd.Function):
+    """h = act(x @ Wg^T) * (x @ Wu^T) for a fused [gate | up] weight w of
+    shape (2I, H), with the activation in the GEMM epilogue ("Fused Kernels",
+    section 4).  The forward keeps the pre-activations [g | u] (written by
+    the same kernel) for the backward, which runs the elementwise backward
+    on them in place ("Kernel Profile: SwiGLU", Backward Pass) and then the
+    two GEMMs of the projection's gradient: dx = d[g|u] @ w and
+    dw = d[g|u]^T @ x (torch matmuls)."""
+
+    @staticmethod
+    def forward(ctx, x, w, kind: str):
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1])
+        need = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
+        if need:
+            h, gu = _glu.glu_gemm_fwd(kind, x2, w, gu=True)
+            ctx.save_for_backward(x2, w, gu)
+        else:
+            h = _glu.glu_gemm_fwd(kind, x2, w)
+        ctx.kind = kind
+        ctx.lead = lead
+        return h.reshape(*lead, h.shape[-1])
+
+    @staticmethod
+    def backward(ctx, dh):
+        x2, w, gu = ctx.saved_tensors
+        dh2 = dh.reshape(-1, dh.shape[-1])
+        if not _row_major(dh2):
+            dh2 = dh2.contiguous()
+        dgu = _glu.glu_bwd(ctx.kind, "gate_up", gu, None, dh2, inplace=True)
+        dx = torch.mm(dgu, w) if ctx.needs_input_grad[0] else None
+        dw = torch.mm(dgu.t(), x2) if ctx.needs_input_grad[1] else None
+        if dx is not None:
+            dx = dx.reshape(*ctx.lead, dx.shape[-1])
+        return dx, dw, None
+
+
+def gate_up_activation(x: torch.Tensor, w: torch.Tensor, kind: str = "silu") -> torch.Tensor:
+    """act(x @ w[:I]^T) * (x @ w[I:]^T) for a fused [gate | up] weight w of
+    shape (2I, H), on the matrix cores with the activation in the epilogue."""
+    if kind not in _KINDS:
+        raise ValueError(f"unknown kind {kind!r}; expected one of {_KINDS}")
+    return FusedGateUpActivation.apply(x, w, kind)
+
+
 def gated_activation(a: torch.Tensor, b: torch.Tensor | None = None, kind: str = "silu",
                      inplace_backward: bool = True) -> torch.Tensor:
     """act(a) * b; with b None, a is the fused [gate | up] tensor."""
@@ -167,15 +212,21 @@ def reglu(a, b=None, inplace_backward: bool = True):
 class GatedMLP(nn.Module):
     """down_proj(act(gate_proj(x)) * up_proj(x)) with the activation step on
     the gfx950 kernels.  fused_gate_up=True keeps gate and up as one
-    projection of width 2*intermediate_size whose output is [gate | up]."""
+    projection of width 2*intermediate_size whose output is [gate | up].
+    fused_epilogue=True (needs fused_gate_up, bf16/fp16) computes that
+    projection and the activation in one kernel (gate_up_activation)."""
 
     def __init__(self, hidden_size: int, intermediate_size: int, kind: str = "silu",
-                 fused_gate_up: bool = True, inplace_backward: bool = True, device=None, dtype=None):
+                 fused_gate_up: bool = True, inplace_backward: bool = True, fused_epilogue: bool = False,
+                 device=None, dtype=None):
         super().__init__()
         if kind not in _KINDS:
             raise ValueError(f"unknown kind {kind!r}")
+        if fused_epilogue and not fused_gate_up:
+            raise ValueError("fused_epilogue needs fused_gate_up=True")
         self.kind = kind
         self.fused_gate_up = fused_gate_up
+        self.fused_epilogue = fused_epilogue
         self.inplace_backward = inplace_backward
         kw = dict(bias=False, device=device, dtype=dtype)
         if fused_gate_up:
@@ -186,6 +237,8 @@ class GatedMLP(nn.Module):
         self.down_proj = nn.Linear(intermediate_size, hidden_size, **kw)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if self.fused_epilogue:
+            return self.down_proj(gate_up_activation(x, self.gate_up_proj.weight, self.kind))
         if self.fused_gate_up:
             h = gated_activation(self.gate_up_proj(x), None, self.kind, self.inplace_backward)
         else:
