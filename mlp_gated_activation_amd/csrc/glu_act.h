@@ -83,17 +83,22 @@ constexpr double kTanhCubic = 0.044715;
 // E is taken from the hardware exponential as Es = E * 2^16 = 2^(16 - x^2 log2(e)/2),
 // which stays normal for |x| < 14 (beyond that Phi(-|x|) and phi are below
 // every bf16/fp16 subnormal); the 2^-16 goes into the final products, which
-// round subnormal results correctly.  One exp serves Phi and phi; relative
-// error of Phi about 1e-6 over all fp16/bf16 inputs; no 1 + erf cancellation.
+// round subnormal results correctly.  One exp serves Phi and phi; no 1 + erf
+// cancellation.  PRECISE (the backward, whose Phi + x phi cancels near its
+// root): Q to 5.6e-7 relative, Phi about 1e-6 over all fp16/bf16 inputs.
+// Otherwise (the forward x Phi(x)): the degree-5 table, Q to 6.5e-5, i.e.
+// at most about 0.13 fp16 ulp of the result before its rounding.
 constexpr float kLog2e = 1.44269504088896341f;
-__device__ inline void norm_cdf(float x, float &Phi, float &phi)
+template <bool PRECISE = true> __device__ inline void norm_cdf(float x, float &Phi, float &phi)
 {
-    constexpr float c[GLU_ERFC_Q_DEG + 1] = GLU_ERFC_Q_COEFFS;
+    constexpr int deg = PRECISE ? GLU_ERFC_Q_DEG : GLU_ERFC_QF_DEG;
+    constexpr float cp[GLU_ERFC_Q_DEG + 1] = GLU_ERFC_Q_COEFFS;
+    constexpr float cf[GLU_ERFC_QF_DEG + 1] = GLU_ERFC_QF_COEFFS;
     const float t = recip(1.0f + fabs_(x) * float(0.5 * kInvSqrt2));
-    float q = c[GLU_ERFC_Q_DEG];
+    float q = PRECISE ? cp[deg] : cf[deg];
 #pragma unroll
-    for (int k = GLU_ERFC_Q_DEG - 1; k >= 0; --k)
-        q = fma_(q, t, c[k]);
+    for (int k = deg - 1; k >= 0; --k)
+        q = fma_(q, t, PRECISE ? cp[k] : cf[k]);
     const float Es = __builtin_amdgcn_exp2f(fma_(x * x, -0.5f * kLog2e, 16.0f));
     const float h = (t * q * 0x1p-17f) * Es;
     Phi = x >= 0.0f ? 1.0f - h : h;
@@ -118,7 +123,7 @@ template <int KIND, typename M> __device__ inline M act(M x)
         // x * Phi(x), Phi(x) = (1 + erf(x/sqrt2))/2 = erfc(-x/sqrt2)/2: reasoning step 7
         if constexpr (sizeof(M) == 4) {
             float Phi, phi;
-            norm_cdf(x, Phi, phi);
+            norm_cdf<false>(x, Phi, phi);
             return x * Phi;
         } else {
             return x * (M(0.5) * erfc_<M>(x * M(-kInvSqrt2)));

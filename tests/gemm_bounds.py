@@ -9,10 +9,11 @@ any order of K fp32 additions is within
 of the exact g (the standard summation bound), and likewise E_u.  So, with
 L = 1.13 >= max |act'| over all four activations (SiLU 1.0998, GELU-erf
 1.1289, GELU-tanh 1.1295, ReLU 1),
-    |h_gpu - h| <= ulp_T(h) + L E_g (|u| + E_u) + |act(g)| E_u + 2^-18 |act(g) u|
-where the last term covers the fp32 evaluation of act and of the product,
-and ulp_T(h) the final rounding (one output ulp, as for the elementwise
-kernels).  The pre-activations written to gu satisfy
+    |h_gpu - h| <= ulp_T(h) + L E_g (|u| + E_u) + |act(g)| E_u + 2^-13 |act(g) u|
+where the last term covers the fp32 evaluation of act and of the product
+(the forward GELU-erf's normal CDF is a polynomial fit to 6.5e-5 relative,
+the other activations are within a few fp32 ulp), and ulp_T(h) the final
+rounding (one output ulp, as for the elementwise kernels).  The pre-activations written to gu satisfy
 |g_gpu - g| <= ulp_T(g) + E_g, and the same for u.
 
 The bound is a worst case: typical accumulation errors grow like sqrt(K)
@@ -41,7 +42,7 @@ def h_bound(fmt: str, K: int, x, wg, wu, h_ref, g_ref, u_ref, act_g):
     Eg = gamma(K) * sums_abs(x, wg)
     Eu = gamma(K) * sums_abs(x, wu)
     return (ulp(h_ref, FORMATS[fmt]) + L_ACT * Eg * (np.abs(u_ref) + Eu) + np.abs(act_g) * Eu
-            + 2.0 ** -18 * np.abs(act_g * u_ref))
+            + 2.0 ** -13 * np.abs(act_g * u_ref))
 
 
 def pre_bound(fmt: str, K: int, x, w, ref):
