@@ -8,10 +8,11 @@
 // through HBM).
 //
 // This is a dense contraction, so it runs on the matrix cores:
-//  - a workgroup of 256 threads (4 waves, 2 x 2) owns 256 rows of x and 128
-//    columns of h, i.e. 128 gate and 128 up rows of the weights; each wave
-//    holds a 128 x 64 block of g and the same block of u in 16 fp32
-//    accumulators of v_mfma_f32_32x32x16_{bf16,f16};
+//  - a workgroup of 512 threads (8 waves, 4 x 2; two per SIMD, so one
+//    wave's LDS and barrier waits are covered by the other's MFMAs) owns
+//    256 rows of x and 128 columns of h, i.e. 128 gate and 128 up rows of the
+//    weights; each wave holds a 64 x 64 block of g and the same block of u in
+//    8 fp32 accumulators of v_mfma_f32_32x32x16_{bf16,f16};
 //  - both operands are k-contiguous (x rows, weight rows), so every MFMA
 //    fragment is one 16-byte LDS read;
 //  - k advances 64 at a time through two LDS stages of 64 KiB; the next
@@ -68,9 +69,16 @@ constexpr int RPI = 1024 / ROW_BYTES;           // rows per wave load instructio
 constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
 constexpr int NST = (128 * 1024) / STAGE_BYTES; // LDS stages (128 KiB in all)
 constexpr int PREF = NST - 1;                   // stages in flight ahead of the one computed
-constexpr int LOADS = 128 / RPI;                // load instructions per wave per stage
+#ifndef GLU_GEMM_WAVES
+#define GLU_GEMM_WAVES 8   // 4 (one wave per SIMD, 128 x 64 per wave) measured 8 % slower
+#endif
+constexpr int WAVES = GLU_GEMM_WAVES;           // (WAVES/2) x 2 waves per workgroup
+constexpr int THREADS = 64 * WAVES;
+constexpr int RPW = ROWS / WAVES;               // stage rows each wave loads
+constexpr int TPW = BM / (WAVES / 2);           // tokens (x rows) each wave computes
+constexpr int LOADS = RPW / RPI;                // load instructions per wave per stage
 constexpr int KSTEPS = BK / KD;                 // MFMA k steps per stage
-constexpr int FX = 128 / MF;                    // x (token) fragments per wave
+constexpr int FX = TPW / MF;                    // x (token) fragments per wave
 constexpr int FW = 64 / MF;                     // gate (and up) fragments per wave
 constexpr int NREAD = FX + 2 * FW;              // fragment reads per k step
 constexpr int NMFMA = FX * 2 * FW;              // MFMAs per k step
@@ -103,7 +111,7 @@ __device__ inline void lds_barrier()
 }
 
 template <typename E, int KIND>
-__global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
+__global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
 {
     __shared__ u32x4 lds_v[NST * STAGE_BYTES / 16];
     char *lds = reinterpret_cast<char *>(lds_v);
@@ -114,9 +122,9 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
 
-    // Loads: wave w fills stage rows [128 w, 128 w + 128): x rows for waves
-    // 0-1, gate rows for wave 2, up rows for wave 3.  Instruction j covers
-    // rows 128 w + RPI j + lane / CPR; lane puts logical chunk
+    // Loads: wave w fills stage rows [RPW w, RPW w + RPW): x rows, then
+    // gate rows, then up rows.  Instruction j covers rows
+    // RPW w + RPI j + lane / CPR; lane puts logical chunk
     // (lane % CPR) ^ swz(row) at position lane % CPR, i.e. at LDS byte
     // row * ROW_BYTES + 16 * (lane % CPR): one contiguous KiB per wave
     // instruction, the layout the direct-to-LDS load writes.  Rows past M or
@@ -128,15 +136,17 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
     const int wu = __builtin_amdgcn_readfirstlane(w);
     const char *gbase;
     int64_t gld, gfirst, glimit;
-    if (wu < 2) {
+    const int r0 = RPW * wu;   // first stage row this wave loads
+    if (r0 < BM) {
         gbase = static_cast<const char *>(p.x);
         gld = p.ldx;
-        gfirst = m0 + 128 * wu;
+        gfirst = m0 + r0;
         glimit = p.M;
     } else {
-        gbase = static_cast<const char *>(wu == 2 ? p.wg : p.wu);
-        gld = wu == 2 ? p.ldwg : p.ldwu;
-        gfirst = n0;
+        const bool gate = r0 < BM + BN;
+        gbase = static_cast<const char *>(gate ? p.wg : p.wu);
+        gld = gate ? p.ldwg : p.ldwu;
+        gfirst = n0 + (gate ? r0 - BM : r0 - BM - BN);
         glimit = p.N;
     }
     const int64_t fc = gfirst < glimit ? gfirst : glimit - 1;
@@ -145,14 +155,14 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
     uint32_t goff[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-        const int r = 128 * wu + RPI * j + lrow;
+        const int r = r0 + RPI * j + lrow;
         int64_t row = gfirst + RPI * j + lrow;
         row = row < glimit ? row : glimit - 1;
         goff[j] = uint32_t(((row - fc) * gld + 8 * (lpos ^ swz(r))) * 2);
     }
     auto issue_direct = [&](int buf, int k0, int j) {
         __builtin_amdgcn_global_load_lds((gbl_t *)(tbase + int64_t(k0) * 2 + uint64_t(goff[j])),
-                                         (lds_t *)(lds + buf * STAGE_BYTES + (128 * wu + RPI * j) * ROW_BYTES), 16,
+                                         (lds_t *)(lds + buf * STAGE_BYTES + (r0 + RPI * j) * ROW_BYTES), 16,
                                          0, 0);
     };
     // The last stage may be partial: zero past K, through registers (the
@@ -160,7 +170,7 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
     auto issue_partial = [&](int buf, int k0) {
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
-            const int r = 128 * wu + RPI * j + lrow;
+            const int r = r0 + RPI * j + lrow;
             const int kc = 8 * (lpos ^ swz(r));
             const u32x4 v = k0 + kc < p.K ? *reinterpret_cast<const u32x4 *>(tbase + int64_t(k0) * 2 + uint64_t(goff[j]))
                                           : u32x4{0, 0, 0, 0};
@@ -181,7 +191,7 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
     // chunk KD/8 * ks + lane / MF; row r, chunk c -> LDS byte
     // r*ROW_BYTES + 16*(c ^ swz(r)).
     const int kq = lane / MF;
-    const int ra = wm * 128 + (lane % MF), rg = BM + wn * 64 + (lane % MF), ru = BM + BN + wn * 64 + (lane % MF);
+    const int ra = wm * TPW + (lane % MF), rg = BM + wn * 64 + (lane % MF), ru = BM + BN + wn * 64 + (lane % MF);
     struct Frags {
         u32x4 a[FX], g[FW], u[FW];
     };
@@ -310,7 +320,7 @@ __global__ void __launch_bounds__(256, 1) gemm_glu_kernel(const GemmArgs p)
     };
 #pragma unroll
     for (int i = 0; i < FX; ++i) {
-        const int64_t m = m0 + wm * 128 + i * MF + (lane % MF);
+        const int64_t m = m0 + wm * TPW + i * MF + (lane % MF);
         if (m >= p.M)
             continue;
         E *hrow = h + m * p.ldh;
@@ -355,7 +365,7 @@ hipError_t launch_gemm_glu(int dtype, int kind, const GemmArgs &args, hipStream_
     GemmFn fn = dtype == F16 ? pick_gemm<_Float16>(kind) : pick_gemm<__bf16>(kind);
     GemmArgs copy = args;
     void *kargs[] = {&copy};
-    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(args.tiles_m * args.tiles_n), dim3(256), kargs, 0,
+    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(args.tiles_m * args.tiles_n), dim3(THREADS), kargs, 0,
                            stream);
 }
 
