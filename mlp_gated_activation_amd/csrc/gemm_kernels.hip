@@ -22,8 +22,8 @@
 //    over the banks; the MFMA fragments of the next 16-deep k step are read
 //    while the current step's MFMAs issue;
 //  - g and u of one element sit in the same lane and register slot, so the
-//    epilogue act(g) * u is lane-local; h is rounded once to the storage type
-//    and leaves four features (8 bytes) per store.
+//    epilogue act(g) * u is lane-local; h is rounded once to the storage type,
+//    staged through LDS and written in whole cache lines.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -298,51 +298,59 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
     // Epilogue.  The MFMAs take the weight rows as their first operand, so
     // each 32 x 32 block is g^T: lane holds token row m = lane % 32 of the
     // block and, for e < 16, feature column 8*(e/4) + 4*(lane/32) + e%4.
-    // Four consecutive features of one token leave as one 8-byte store.
-    E *h = static_cast<E *>(p.h);
-    E *gu = static_cast<E *>(p.gu);
+    // Each output tile (h, then g and u when asked for) is staged through
+    // LDS, now free, as 256 token rows of 128 features (rows padded to 272
+    // bytes), and leaves in 16-byte stores, 16 lanes per 256-byte token row:
+    // whole cache lines, where direct 8-byte stores from the MFMA layout
+    // would leave partial lines.
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    auto put4 = [&](E *base, int64_t n, const float *v) {
-        // 4 values for columns n .. n+3 of one row (masked at N)
-        if (n + 3 < p.N && (reinterpret_cast<uintptr_t>(base + n) & 7) == 0) {
-            typedef E ex4 __attribute__((ext_vector_type(4)));
-            ex4 q;
+    typedef E ex4 __attribute__((ext_vector_type(4)));
+    constexpr int OPITCH = BN * 2 + 16;   // bytes per staged token row
+    static_assert(BM * OPITCH <= NST * STAGE_BYTES, "output tile fits the stage buffers");
+    auto put = [&](E *dst, int64_t ld, auto value) {
+        // this wave's values -> LDS
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                q[t] = static_cast<E>(v[t]);
-            *reinterpret_cast<u32x2 *>(base + n) = __builtin_bit_cast(u32x2, q);
-        } else {
+        for (int i = 0; i < FX; ++i)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                if (n + t < p.N)
-                    base[n + t] = static_cast<E>(v[t]);
-        }
-    };
+            for (int j = 0; j < FW; ++j)
 #pragma unroll
-    for (int i = 0; i < FX; ++i) {
-        const int64_t m = m0 + wm * TPW + i * MF + (lane % MF);
-        if (m >= p.M)
-            continue;
-        E *hrow = h + m * p.ldh;
+                for (int q = 0; q < ACC_E / 4; ++q) {
+                    ex4 v4;
 #pragma unroll
-        for (int j = 0; j < FW; ++j)
-#pragma unroll
-            for (int q = 0; q < ACC_E / 4; ++q) {
-                // features of registers 4q .. 4q+3: 8q + 4*(lane/32) + t
-                const int64_t n = n0 + wn * 64 + j * MF + q * 8 + (lane >> 5) * 4;
-                float hv[4], gv[4], uv[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    gv[t] = accg[i][j][4 * q + t];
-                    uv[t] = accu[i][j][4 * q + t];
-                    hv[t] = act<KIND, float>(gv[t]) * uv[t];
+                    for (int t = 0; t < 4; ++t)
+                        v4[t] = static_cast<E>(value(i, j, 4 * q + t));
+                    const int row = wm * TPW + i * MF + (lane % MF);
+                    const int col = wn * 64 + j * MF + q * 8 + (lane >> 5) * 4;
+                    *reinterpret_cast<u32x2 *>(lds + row * OPITCH + col * 2) = __builtin_bit_cast(u32x2, v4);
                 }
-                put4(hrow, n, hv);
-                if (gu) {
-                    put4(gu + m * p.ldgu, n, gv);
-                    put4(gu + m * p.ldgu + p.N, n, uv);
-                }
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        // LDS -> memory: chunk c covers token row c / 16, features 8 (c % 16) .. + 7
+#pragma unroll
+        for (int k = 0; k < BM * BN / 8 / THREADS; ++k) {
+            const int c = tid + THREADS * k, row = c >> 4, col = (c & 15) * 8;
+            const int64_t m = m0 + row, n = n0 + col;
+            if (m >= p.M || n >= p.N)
+                continue;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + row * OPITCH + col * 2);
+            E *out = dst + m * ld + n;
+            if (n + 8 <= p.N && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+                *reinterpret_cast<u32x4 *>(out) = v;
+            } else {
+                const E *e = reinterpret_cast<const E *>(&v);
+                for (int t = 0; t < 8 && n + t < p.N; ++t)
+                    out[t] = e[t];
             }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();   // the tile is out of LDS before the next one goes in
+    };
+    put(static_cast<E *>(p.h), p.ldh,
+        [&](int i, int j, int e) { return act<KIND, float>(accg[i][j][e]) * accu[i][j][e]; });
+    if (p.gu) {
+        E *gu = static_cast<E *>(p.gu);
+        put(gu, p.ldgu, [&](int i, int j, int e) { return accg[i][j][e]; });
+        put(gu + p.N, p.ldgu, [&](int i, int j, int e) { return accu[i][j][e]; });
     }
 }
 
