@@ -20,7 +20,9 @@
 //    write instructions) while the current stage's MFMAs run; stage rows are
 //    128 bytes with XOR-swizzled 16-byte chunks so fragment reads spread
 //    over the banks; the MFMA fragments of the next 16-deep k step are read
-//    while the current step's MFMAs issue;
+//    while the current step's MFMAs issue, and the one barrier per stage sits
+//    before the stage's last MFMAs, which cover it and the first fragment
+//    reads of the next stage;
 //  - g and u of one element sit in the same lane and register slot, so the
 //    epilogue act(g) * u is lane-local; h is rounded once to the storage type,
 //    staged through LDS and written in whole cache lines.
@@ -67,8 +69,7 @@ constexpr int ROW_BYTES = BK * 2;               // one row of a stage
 constexpr int CPR = BK / 8;                     // 16-byte chunks per row
 constexpr int RPI = 1024 / ROW_BYTES;           // rows per wave load instruction (1 KiB)
 constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
-constexpr int NST = (128 * 1024) / STAGE_BYTES; // LDS stages (128 KiB in all)
-constexpr int PREF = NST - 1;                   // stages in flight ahead of the one computed
+constexpr int NST = (128 * 1024) / STAGE_BYTES; // LDS stages (128 KiB in all), all in flight
 #ifndef GLU_GEMM_WAVES
 #define GLU_GEMM_WAVES 8   // 4 (one wave per SIMD, 128 x 64 per wave) measured 8 % slower
 #endif
@@ -83,6 +84,7 @@ constexpr int FW = 64 / MF;                     // gate (and up) fragments per w
 constexpr int NREAD = FX + 2 * FW;              // fragment reads per k step
 constexpr int NMFMA = FX * 2 * FW;              // MFMAs per k step
 static_assert(NST >= 2 && NST <= 4, "two to four stages");
+static_assert(KSTEPS % 2 == 0, "fragment double buffer alternates within a stage");
 
 // Chunk c of stage row r sits at position c ^ swz(r) of the row.  The 16
 // lanes one LDS cycle serves read 16 consecutive rows at one logical chunk;
@@ -217,49 +219,13 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
                 accu[i][j] = MfmaOp<E>::run(f.u[j], f.a[i], accu[i][j]);
             }
     };
-    // One stage: KSTEPS 16-deep steps.  The fragments of step ks + 1 are
-    // read while step ks's 16 MFMAs issue; with `direct`, the loads of a
-    // later stage go straight into LDS during the first step.
-    auto stage = [&](const char *st, bool direct, int nbuf, int k1) {
-        Frags f[2];
-        read(st, 0, f[0]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            if (ks == 0 && direct) {
-#pragma unroll
-                for (int j = 0; j < LOADS; ++j)
-                    issue_direct(nbuf, k1, j);
-            }
-            if (ks + 1 < KSTEPS)
-                read(st, ks + 1, f[(ks + 1) & 1]);
-            mfmas(f[ks & 1]);
-            if (ks + 1 < KSTEPS) {
-#pragma unroll
-                for (int q = 0; q < NREAD; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-                    if (ks == 0 && direct)
-                        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (LOADS + NREAD - 1) / NREAD, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NREAD, 0);
-            } else {
-                if (ks == 0 && direct)
-                    for (int q = 0; q < LOADS; ++q) {
-                        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-                    }
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA, 0);
-            }
-            // nothing crosses between steps: each step's MFMAs use only
-            // fragments read one step earlier
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
     // Wait until at most `ahead` later stages of this wave's loads are in
-    // flight, then barrier: the stage about to be computed is in LDS.
+    // flight and this wave's LDS reads are done, then barrier: the next stage
+    // is in LDS, and no wave still reads the buffer about to be refilled.
     auto wait_stage = [&](int ahead) {
-        if (ahead >= 2)
+        if (ahead >= 3)   // at most NST - 1 <= 3
+            __builtin_amdgcn_s_waitcnt(vm_wait<3 * LOADS>());
+        else if (ahead == 2)
             __builtin_amdgcn_s_waitcnt(vm_wait<2 * LOADS>());
         else if (ahead == 1)
             __builtin_amdgcn_s_waitcnt(vm_wait<LOADS>());
@@ -270,28 +236,76 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
     };
 
     const int KT = (p.K + BK - 1) / BK, KF = p.K / BK;   // stages, full stages
-    // Prologue: the first PREF stages.
+    // Steps 0 .. KSTEPS-2 of a stage: the fragments of step ks + 1 are read
+    // while step ks's MFMAs issue.
+    auto steps = [&](const char *st, Frags *f) {
 #pragma unroll
-    for (int s = 0; s < PREF; ++s) {
+        for (int ks = 0; ks + 1 < KSTEPS; ++ks) {
+            read(st, ks + 1, f[(ks + 1) & 1]);
+            mfmas(f[ks & 1]);
+#pragma unroll
+            for (int q = 0; q < NREAD; ++q) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NREAD, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Prologue: every buffer, then stage 0's first fragments.  A buffer is
+    // refilled only once its own stage has been read, so all NST stages are
+    // in flight together.
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
         if (s < KF)
             for (int j = 0; j < LOADS; ++j)
                 issue_direct(s, s * BK, j);
         else if (s < KT)
             issue_partial(s, s * BK);
     }
-    int kt = 0;
-    // Main loop: the stage PREF ahead is a full one, fetched directly into LDS.
-    for (; kt + PREF < KF; ++kt) {
-        wait_stage(PREF - 1);
-        stage(lds + (kt % NST) * STAGE_BYTES, true, (kt + PREF) % NST, (kt + PREF) * BK);
-    }
-    // The remaining stages; the partial one (if any) goes through registers.
-    for (; kt < KT; ++kt) {
-        const int ahead = KT - 1 - kt < PREF - 1 ? KT - 1 - kt : PREF - 1;
+    Frags f[2];
+    {
+        const int ahead = KT - 1 < NST - 1 ? KT - 1 : NST - 1;
         wait_stage(ahead);
-        if (kt + PREF < KT)
-            issue_partial((kt + PREF) % NST, (kt + PREF) * BK);
-        stage(lds + (kt % NST) * STAGE_BYTES, false, 0, 0);
+        read(lds, 0, f[0]);
+    }
+    // The barrier of stage kt + 1 sits inside stage kt's last step, between
+    // its fragment reads (done: the fragments are in registers) and its MFMAs,
+    // which then cover the barrier, the loads into the buffer just freed
+    // (stage kt's own) and the fragment reads of stage kt + 1's first step.
+    int kt = 0;
+    for (; kt + NST < KF; ++kt) {
+        steps(lds + (kt % NST) * STAGE_BYTES, f);
+        wait_stage(NST - 2);
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j)
+            issue_direct(kt % NST, (kt + NST) * BK, j);
+        read(lds + ((kt + 1) % NST) * STAGE_BYTES, 0, f[0]);
+        mfmas(f[1]);
+#pragma unroll
+        for (int q = 0; q < NREAD; ++q) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (LOADS + NREAD - 1) / NREAD, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NREAD, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; kt < KT; ++kt) {
+        steps(lds + (kt % NST) * STAGE_BYTES, f);
+        if (kt + 1 < KT) {
+            const int ahead = KT - 2 - kt < NST - 2 ? KT - 2 - kt : NST - 2;
+            wait_stage(ahead);
+            const int s = kt + NST;
+            if (s < KF)
+                for (int j = 0; j < LOADS; ++j)
+                    issue_direct(kt % NST, s * BK, j);
+            else if (s < KT)
+                issue_partial(kt % NST, s * BK);
+            read(lds + ((kt + 1) % NST) * STAGE_BYTES, 0, f[0]);
+        }
+        mfmas(f[1]);
+        __builtin_amdgcn_sched_barrier(0);
     }
     lds_barrier();
 
