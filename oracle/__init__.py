@@ -75,6 +75,8 @@ def _load():
         lib.oracle_gemm_glu.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -98,6 +100,11 @@ def _ptr(x: np.ndarray):
 def num_threads() -> int:
     """OpenMP threads the element loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Sets the OpenMP threads of the element loops (n >= 1)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def act1(kind, x: float) -> float:

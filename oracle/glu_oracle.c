@@ -238,10 +238,13 @@ void oracle_gemm_glu(int kind, int64_t M, int64_t N, int64_t K, const double *x,
     }
 }
 
-/* Thread count OpenMP will use for the loops above (1 without OpenMP). */
+/* Thread count OpenMP will use for the loops above (1 without OpenMP), and
+ * a way to change it (n >= 1) for single-thread timings. */
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { omp_set_num_threads(n < 1 ? 1 : n); }
 #else
 int oracle_num_threads(void) { return 1; }
+void oracle_set_num_threads(int n) { (void)n; }
 #endif
