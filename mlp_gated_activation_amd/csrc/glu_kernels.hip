@@ -486,7 +486,15 @@ hipError_t launch_tiles(int dtype, int kind, bool backward, const TileArgs &args
                              : (backward ? pick_tile<SBf16, true>(kind) : pick_tile<SBf16, false>(kind));
     TileArgs copy = args;
     void *kargs[] = {&copy};
-    const size_t lds = size_t(args.nslots) * kTile * (kTile + 1) * sizeof(float);
+    // The slots the launch needs, but at least kTileMinLds: that caps the
+    // tiled kernels at five workgroups per CU.  The forward kernels' register
+    // count would allow eight, and the extra tiles in flight only slow the
+    // transposed stores (forward into a transposed y at 4096 x 14336 bf16:
+    // 4754 GB/s uncapped, 5397 at five per CU, 3695 at two); the backward
+    // kernels' registers already cap them at five.
+    constexpr size_t kTileMinLds = 32 * 1024;
+    size_t lds = size_t(args.nslots) * kTile * (kTile + 1) * sizeof(float);
+    lds = lds < kTileMinLds ? kTileMinLds : lds;
     return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(ntiles), dim3(256), kargs, lds, stream);
 }
 
