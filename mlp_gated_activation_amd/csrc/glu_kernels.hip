@@ -491,7 +491,7 @@ hipError_t launch_tiles(int dtype, int kind, bool backward, const TileArgs &args
     // count would allow eight, and the extra tiles in flight only slow the
     // transposed stores (forward into a transposed y at 4096 x 14336 bf16:
     // 4754 GB/s uncapped, 5397 at five per CU, 3695 at two); the backward
-    // kernels' registers already cap them at five.
+    // kernels' registers already cap them at four.
     constexpr size_t kTileMinLds = 32 * 1024;
     size_t lds = size_t(args.nslots) * kTile * (kTile + 1) * sizeof(float);
     lds = lds < kTileMinLds ? kTileMinLds : lds;
