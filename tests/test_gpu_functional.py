@@ -114,6 +114,7 @@ def _reference_mlp(x, wgu, wd, kind, fused, inter):
 
 def _rel(got, ref):
     got = got.detach().cpu().double()
+    ref = ref.detach().double()
     return float((got - ref).norm() / ref.norm())
 
 
