@@ -95,12 +95,16 @@ template <bool PRECISE = true> __device__ inline void norm_cdf(float x, float &P
     constexpr float cp[GLU_ERFC_Q_DEG + 1] = GLU_ERFC_Q_COEFFS;
     constexpr float cf[GLU_ERFC_QF_DEG + 1] = GLU_ERFC_QF_COEFFS;
     const float t = recip(1.0f + fabs_(x) * float(0.5 * kInvSqrt2));
-    float q = PRECISE ? cp[deg] : cf[deg];
+    // Q's coefficients carry the 2^-17 that undoes the exponent offset below:
+    // scaling by a power of two commutes with every rounding here (all values
+    // stay normal), so this equals scaling t*Q afterwards, one multiply less.
+    constexpr float kS = 0x1p-17f;
+    float q = (PRECISE ? cp[deg] : cf[deg]) * kS;
 #pragma unroll
     for (int k = deg - 1; k >= 0; --k)
-        q = fma_(q, t, PRECISE ? cp[k] : cf[k]);
+        q = fma_(q, t, (PRECISE ? cp[k] : cf[k]) * kS);
     const float Es = __builtin_amdgcn_exp2f(fma_(x * x, -0.5f * kLog2e, 16.0f));
-    const float h = (t * q * 0x1p-17f) * Es;
+    const float h = (t * q) * Es;
     Phi = x >= 0.0f ? 1.0f - h : h;
     phi = Es * float(kInvSqrt2Pi * 0x1p-16);
 }
