@@ -17,7 +17,8 @@
 //  - rows are addressed through row strides with one multiply-high division
 //    per 16-byte unit, never a per-element divide ([SWIGLU] "Performance
 //    requirements", interleaved layout cost);
-//  - there is no LDS, no cross-lane traffic and no MFMA.
+//  - there is no LDS traffic, no cross-lane traffic and no MFMA (the light
+//    16-bit kinds reserve LDS only to cap the workgroups per CU; see launch).
 // Math: bf16/fp16 are widened to fp32, fp32 to fp64; the result is rounded
 // once at the store ([SWIGLU] "Kernel design rules").
 #include <hip/hip_runtime.h>
