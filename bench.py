@@ -177,6 +177,8 @@ def main():
                     help="skip the torch eager comparison")
     ap.add_argument("--no-copy-check", dest="copy_check", action="store_false",
                     help="skip the torch device-copy reference")
+    ap.add_argument("--torch-compile", action="store_true",
+                    help="also time torch.compile of the same step (context; compiles on first use)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -278,6 +280,42 @@ def main():
                  "speedup_step": round(t_es / ms_per_step, 2),
                  "note": "F.silu(a) * b and autograd, bf16, same buffers; algorithmic bytes / time"}
 
+    # Context: torch.compile of the same step, the other comparison provider
+    # the pages name ("Write a Triton SiLU-Mul (SwiGLU) Kernel", Performance
+    # requirements: a custom kernel should beat it clearly).  Opt-in: it
+    # compiles on first use.
+    compiled = None
+    if args.torch_compile:
+        import torch.nn.functional as F
+        try:
+            reps = min(args.steps, 100)
+            cfwd = torch.compile(lambda a, b: F.silu(a) * b, dynamic=False)
+
+            def comp_fwd(i):
+                a, b, dy, y = sets[i % len(sets)]
+                cfwd(a, b)
+
+            def comp_step(i):
+                a, b, dy, y = sets[i % len(sets)]
+                a_ = a.detach().requires_grad_()
+                b_ = b.detach().requires_grad_()
+                cfwd(a_, b_).backward(dy)
+
+            t0 = time.perf_counter()
+            for i in range(5):
+                comp_fwd(i)
+                comp_step(i)
+            torch.cuda.synchronize()
+            t_compile = time.perf_counter() - t0
+            t_cf = timed(comp_fwd, reps) / reps
+            t_cs = timed(comp_step, reps) / reps
+            compiled = {"fwd_us": round(1e3 * t_cf, 2), "fwd_GBps": round(FWD_BYTES / (t_cf * 1e-3) / 1e9, 1),
+                        "step_us": round(1e3 * t_cs, 2), "step_GBps": round(STEP_BYTES / (t_cs * 1e-3) / 1e9, 1),
+                        "speedup_step": round(t_cs / ms_per_step, 2), "first_calls_s": round(t_compile, 1),
+                        "note": "torch.compile(F.silu(a) * b), forward and autograd backward, bf16, same buffers"}
+        except Exception as e:   # context only: report, do not fail the benchmark
+            compiled = {"error": f"{type(e).__name__}: {e}"[:300]}
+
     # attainable reference: a plain device copy (1 read + 1 write) of the same bytes
     copy = copy_reference(torch, dev, stream) if args.copy_check else None
 
@@ -310,6 +348,7 @@ def main():
         },
         "torch_copy_GBps": copy,
         "torch_eager": eager,
+        "torch_compile": compiled,
         "wall_s_timed": round(wall, 4),
         "roofline": {
             "bound": "hbm",
