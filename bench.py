@@ -162,12 +162,13 @@ def copy_reference(torch, dev, stream):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=["glu", "add_rmsnorm", "glu_strided", "gemm_glu"], default="glu",
+    ap.add_argument("--op", choices=["glu", "add_rmsnorm", "glu_strided", "gemm_glu", "providers"], default="glu",
                     help="glu: the SwiGLU fwd+bwd step (default); add_rmsnorm: the fused residual "
                          "add + RMSNorm forward, bf16, 4096 rows; glu_strided: the SwiGLU backward "
                          "with a transposed incoming gradient (LDS-tiled kernel) and related layouts; "
                          "gemm_glu: the gate/up projection with the activation fused into its epilogue "
-                         "(bf16, 4096 tokens, hidden 4096, I 14336)")
+                         "(bf16, 4096 tokens, hidden 4096, I 14336); providers: the SwiGLU op at "
+                         "4096 x H, H = 1024 .. 16384, against torch eager and torch.compile")
     ap.add_argument("--hidden", type=int, default=4096, help="add_rmsnorm only: row width")
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
@@ -205,6 +206,8 @@ def main():
         return bench_strided(args, torch, glu, inputs, dev)
     if args.op == "gemm_glu":
         return bench_gemm(args, torch, glu, inputs, dev)
+    if args.op == "providers":
+        return bench_providers(args, torch, glu, inputs, dev)
     w = inputs.WORKLOADS["swiglu_bf16_4096x14336"]
     a_h, b_h, dy_h = w.make(seed=0)
     sets = []
@@ -365,6 +368,133 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(a_h, b_h, dy_h)
+    print(json.dumps(result), flush=True)
+
+
+def bench_providers(args, torch, glu, inputs, dev):
+    """The SwiGLU op over the pages' benchmark sweep ("LigerSiLUMulFunction",
+    Benchmarking: hidden size 1024 .. 16384, 4096 rows, bf16; providers this
+    library, torch eager and torch.compile), forward and full (forward then
+    backward).  Every provider is launched call by call from Python, as a
+    training loop would; for this library a HIP graph of the same calls is
+    timed as well.  Buffer sets rotate over at least 1 GiB, so every call
+    streams from HBM.  Context only: the headline is the default op."""
+    import torch.nn.functional as F
+    stream = torch.cuda.current_stream(dev)
+    reps = min(args.steps, 200)
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    rows_out = []
+    compile_error = None
+    for h in (1024, 2048, 4096, 8192, 16384):
+        # a fresh compilation per size: the guard cache of one compiled
+        # function would otherwise fill up and fall back to eager silently
+        try:
+            torch._dynamo.reset()
+            cfwd = torch.compile(lambda a, b: F.silu(a) * b, dynamic=False)
+        except Exception as e:   # context only
+            cfwd, compile_error = None, f"{type(e).__name__}: {e}"[:300]
+        w = inputs.WORKLOADS[f"swiglu_bf16_4096x{h}"]
+        a_h, b_h, dy_h = w.make(seed=0)
+        n = a_h.numel()
+        nsets = max(2, -(-(1 << 30) // (4 * n * 2)))
+        sets = [[a_h.to(dev), b_h.to(dev), dy_h.to(dev), torch.empty_like(a_h, device=dev)] for _ in range(nsets)]
+        fwd_bytes, step_bytes = 3 * n * 2, 8 * n * 2
+
+        def ours_fwd(i):
+            a, b, dy, y = sets[i % nsets]
+            glu.glu_fwd("silu", "separate", a, b, y)
+
+        def ours_step(i):
+            a, b, dy, y = sets[i % nsets]
+            glu.glu_fwd("silu", "separate", a, b, y)
+            glu.glu_bwd("silu", "separate", a, b, dy, inplace=True)
+
+        def eager_fwd(i):
+            a, b, dy, y = sets[i % nsets]
+            F.silu(a) * b
+
+        def eager_step(i):
+            a, b, dy, y = sets[i % nsets]
+            a_ = a.detach().requires_grad_()
+            b_ = b.detach().requires_grad_()
+            (F.silu(a_) * b_).backward(dy)
+
+        def comp_fwd(i):
+            a, b, dy, y = sets[i % nsets]
+            cfwd(a, b)
+
+        def comp_step(i):
+            a, b, dy, y = sets[i % nsets]
+            a_ = a.detach().requires_grad_()
+            b_ = b.detach().requires_grad_()
+            cfwd(a_, b_).backward(dy)
+
+        def graph_of(fn):
+            """A HIP graph of one call per buffer set; returns the time per call."""
+            fn(0)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(nsets):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+            r = max(1, reps // nsets)
+            return timed(lambda i: g.replay(), r) / nsets
+
+        row = {"H": h, "bytes_fwd": fwd_bytes, "bytes_full": step_bytes}
+        legs = [("ours", ours_fwd, ours_step), ("torch", eager_fwd, eager_step)]
+        if cfwd is not None:
+            legs.append(("torch_compile", comp_fwd, comp_step))
+        for name, f_fwd, f_step in legs:
+            try:
+                for i in range(5):
+                    f_fwd(i)
+                    f_step(i)
+                t_f, t_s = timed(f_fwd, reps), timed(f_step, reps)
+                row[name] = {"fwd_us": round(1e3 * t_f, 2), "full_us": round(1e3 * t_s, 2),
+                             "fwd_GBps": round(fwd_bytes / (t_f * 1e-3) / 1e9, 1),
+                             "full_GBps": round(step_bytes / (t_s * 1e-3) / 1e9, 1)}
+            except Exception as e:   # context only: report, do not fail the sweep
+                row[name] = {"error": f"{type(e).__name__}: {e}"[:300]}
+        t_f, t_s = graph_of(ours_fwd), graph_of(ours_step)
+        row["ours_hip_graph"] = {"fwd_us": round(1e3 * t_f, 2), "full_us": round(1e3 * t_s, 2),
+                                 "fwd_GBps": round(fwd_bytes / (t_f * 1e-3) / 1e9, 1),
+                                 "full_GBps": round(step_bytes / (t_s * 1e-3) / 1e9, 1)}
+        rows_out.append(row)
+        print(f"providers: H={h} done", file=sys.stderr, flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    top = rows_out[-1]
+    result = {
+        "metric": "achieved HBM GB/s, SwiGLU fwd+bwd, bf16, 4096 x H (providers sweep)",
+        "value": top["ours"].get("full_GBps"),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": 5,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded a~N(0,4), b,dy~N(0,1) rounded to bf16; >= 1 GiB of rotating buffer sets)",
+        "config": {"workload": "SwiGLU bf16 separate a,b,dy (4096, H), H = 1024 .. 16384; value at H = 16384",
+                   "providers": ["ours", "torch", "torch_compile", "ours_hip_graph"]},
+        "sweep": rows_out,
+    }
+    if compile_error is not None:
+        result["torch_compile_error"] = compile_error
     print(json.dumps(result), flush=True)
 
 

@@ -108,13 +108,39 @@ def _check(tensors, dtype, device):
             raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+# The current stream's raw handle without building a Stream object (a few
+# microseconds per call, which is most of a small launch's host cost).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device, stream):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class _NoGuard:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
+_NO_GUARD = _NoGuard()
+
+
+def _on(device):
+    """Make `device` current for the launch; a no-op when it already is."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return _NO_GUARD
+    return torch.cuda.device(device)
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def glu_fwd(kind: str, layout: str, a: torch.Tensor, b: torch.Tensor | None = None,
@@ -159,7 +185,7 @@ def glu_fwd(kind: str, layout: str, a: torch.Tensor, b: torch.Tensor | None = No
         y2 = _rows(y, "y")
     _check([("b", b), ("y", y)], a.dtype, a.device)
     rows = a2.shape[0]
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         st = _lib.glu_fwd(k, lay, dt, rows, cols,
                           _ptr(a2), _ld(a2),
                           _ptr(b2), _ld(b2) if b2 is not None else 0,
@@ -223,7 +249,7 @@ def glu_bwd(kind: str, layout: str, a: torch.Tensor, b: torch.Tensor | None, dy:
             result = da
     _check([("b", b), ("dy", dy), ("da", da), ("db", db)], a.dtype, a.device)
     rows = a2.shape[0]
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         st = _lib.glu_bwd(k, lay, dt, rows, cols,
                           _ptr(a2), _ld(a2),
                           _ptr(b2), _ld(b2) if b2 is not None else 0,
@@ -271,7 +297,7 @@ def glu_add_rmsnorm_fwd(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Te
         raise ValueError("rstd must be a contiguous float32 tensor with one value per row")
     x2, r2, h2, y2 = (_rows(t, n) for t, n in ((x, "x"), (residual, "residual"), (h, "h"), (y, "y")))
     rows = x2.shape[0] if x.dim() > 0 else 0
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         st = _lib.glu_add_rmsnorm_fwd(dt, rows, hidden, _ptr(x2), _ld(x2), _ptr(r2), _ld(r2), _ptr(gamma),
                                       _ptr(h2), _ld(h2), _ptr(y2), _ld(y2), _ptr(rstd), float(eps),
                                       _stream(x.device, stream))
@@ -320,7 +346,7 @@ def glu_fwd_strided(kind: str, a: torch.Tensor, b: torch.Tensor, y: torch.Tensor
         y = torch.empty_like(a)
     rows, cols, _, _ = _view2(a, "a")
     ops = _strided_operands([("a", a), ("b", b), ("y", y)], a.shape, a.dtype, a.device)
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         st = _lib.glu_fwd_strided(k, dt, rows, cols, *ops, _stream(a.device, stream))
     if st != 0:
         raise GluError(st, "glu_fwd_strided")
@@ -341,7 +367,7 @@ def glu_bwd_strided(kind: str, a: torch.Tensor, b: torch.Tensor, dy: torch.Tenso
     rows, cols, _, _ = _view2(a, "a")
     ops = _strided_operands([("a", a), ("b", b), ("dy", dy), ("da", da), ("db", db)], a.shape, a.dtype,
                             a.device)
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         st = _lib.glu_bwd_strided(k, dt, rows, cols, *ops, _stream(a.device, stream))
     if st != 0:
         raise GluError(st, "glu_bwd_strided")
@@ -390,7 +416,7 @@ def glu_gemm_fwd(kind: str, x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.T
     gu2 = _rows(gu, "gu") if gu is not None else None
     _check([("w_gate", w_gate), ("w_up", w_up), ("h", h), ("gu", gu)], x.dtype, x.device)
     M = x2.shape[0]
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         st = _lib.glu_gemm_fwd(k, dt, M, N, K, _ptr(x2), _ld(x2), _ptr(wg2), _ld(wg2), _ptr(wu2), _ld(wu2),
                                _ptr(h2), _ld(h2), _ptr(gu2), _ld(gu2) if gu2 is not None else 0,
                                _stream(x.device, stream))
