@@ -25,8 +25,7 @@ enum Kind { SILU = 0, GELU_ERF = 1, GELU_TANH = 2, RELU = 3 };
 // Derivatives are arranged so the one cancellation left (near act''s
 // negative root) is a single well-conditioned sum.
 // ---------------------------------------------------------------------------
-__device__ inline float recip(float x) { return __builtin_amdgcn_rcpf(x); }   // x in [1, 2]
-__device__ inline double recip(double x) { return 1.0 / x; }
+__device__ inline float recip(float x) { return __builtin_amdgcn_rcpf(x); }   // x >= 1
 __device__ inline float fabs_(float x) { return __builtin_fabsf(x); }
 __device__ inline double fabs_(double x) { return __builtin_fabs(x); }
 __device__ inline float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
@@ -36,17 +35,16 @@ __device__ inline double fma_(double a, double b, double c) { return __builtin_f
 // exponential (exp2f keeps subnormal results).  Rounding x*log2(e) to fp32
 // costs a relative error of about |x| * 6e-8 (under 4e-6 wherever a bf16 or
 // fp16 result is not zero), far inside half an output ulp (2^-9 / 2^-12).
-// The fp64 math of fp32 data uses the library exp.
 // Sigmoid pieces from a = |x| (or |w|) >= 0:  e = exp(-a), q = 1/(1 + e).
 // fp32 (bf16/fp16 data): es = e * 2^16 = 2^(16 - a log2(e)) from the raw
 // hardware exponential; es is normal for a < 98.4, and beyond that every
 // product with e is below half the smallest bf16/fp16 subnormal, so the
 // hardware's flush to zero there is harmless.  Rounding the argument near 16
-// costs at most 6.6e-7 relative in e.  fp64 (fp32 data): library exp.
+// costs at most 6.6e-7 relative in e.  fp64 (fp32 data): see below.
 struct SigParts {
     float e, q;
 };
-__device__ inline SigParts sig_parts(float a)
+template <bool PRECISE = true> __device__ inline SigParts sig_parts(float a)
 {
 #if GLU_SCALED_EXP
     const float es = __builtin_amdgcn_exp2f(__builtin_fmaf(a, -1.44269504088896341f, 16.0f));
@@ -56,21 +54,52 @@ __device__ inline SigParts sig_parts(float a)
     return SigParts{e, __builtin_amdgcn_rcpf(1.0f + e)};
 #endif
 }
+// fp64 (fp32 data).  exp(-a) = 2^k * exp(r), k = rint(-a log2 e), with
+// r = -a - k ln2 reduced in two steps (ln2 = L1 + L2, L1 with 32 significant
+// bits, so k * L1 is exact for the |k| <= 1587 here and the first step is an
+// exact difference), |r| <= ln2/2 + 2^-40; exp(r) by its Taylor polynomial.
+// PRECISE (the backward): degree 12, truncation below |r|^13/13! * e^|r| <
+// 3e-16 relative, so e carries a few fp64 ulps of error like a library exp,
+// and the sums that cancel near act''s root, (1 + e) + x and its tanh form,
+// stay as accurate as in exact arithmetic to within fp32 rounding.
+// Otherwise (the forwards, whose products do not cancel): degree 8, below
+// |r|^9/9! * e^|r| < 3e-10 relative, far inside fp32's 2^-24.
+// a >= 0 is clamped to 1100, where exp(-a) is already 0 in fp64; NaN also
+// goes to the clamp, so callers keep NaN through their product with x.
+template <bool PRECISE> __device__ inline double exp_neg(double a)
+{
+    constexpr double kLog2eD = 1.4426950408889634074;
+    constexpr double kLn2Hi = 6.93147180369123816490e-01, kLn2Lo = 1.90821492927058770002e-10;
+    const double ac = a < 1100.0 ? a : 1100.0;
+    const double k = __builtin_rint(ac * -kLog2eD);
+    double r = __builtin_fma(k, -kLn2Hi, -ac);
+    r = __builtin_fma(k, -kLn2Lo, r);
+    constexpr double c[13] = {1.0, 1.0, 1.0 / 2, 1.0 / 6, 1.0 / 24, 1.0 / 120, 1.0 / 720, 1.0 / 5040,
+                              1.0 / 40320, 1.0 / 362880, 1.0 / 3628800, 1.0 / 39916800, 1.0 / 479001600};
+    constexpr int deg = PRECISE ? 12 : 8;
+    double p = c[deg];
+#pragma unroll
+    for (int i = deg - 1; i >= 0; --i)
+        p = __builtin_fma(p, r, c[i]);
+    return __builtin_ldexp(p, int(k));
+}
+// 1/d for d >= 1: the hardware reciprocal and two Newton steps; each squares
+// the relative error, so even a seed within 2^-8 ends below 2^-32.
+__device__ inline double recip_ge1(double d)
+{
+    double q = __builtin_amdgcn_rcp(d);
+    q = __builtin_fma(q, __builtin_fma(-d, q, 1.0), q);
+    return __builtin_fma(q, __builtin_fma(-d, q, 1.0), q);
+}
 struct SigPartsD {
     double e, q;
 };
-__device__ inline SigPartsD sig_parts(double a)
+template <bool PRECISE = true> __device__ inline SigPartsD sig_parts(double a)
 {
-    const double e = exp(-a);
-    return SigPartsD{e, 1.0 / (1.0 + e)};
+    const double e = exp_neg<PRECISE>(a);
+    return SigPartsD{e, recip_ge1(1.0 + e)};
 }
 
-template <typename M> __device__ inline M ex(M x);
-template <> __device__ inline float ex<float>(float x) { return exp2f(x * 1.44269504088896341f); }
-template <> __device__ inline double ex<double>(double x) { return exp(x); }
-template <typename M> __device__ inline M erfc_(M x);
-template <> __device__ inline float erfc_<float>(float x) { return erfcf(x); }
-template <> __device__ inline double erfc_<double>(double x) { return erfc(x); }
 
 constexpr double kInvSqrt2 = 0.70710678118654752440;      // [SWIGLU] reasoning step 7
 constexpr double kInvSqrt2Pi = 0.39894228040143267794;
@@ -109,6 +138,47 @@ template <bool PRECISE = true> __device__ inline void norm_cdf(float x, float &P
     phi = Es * float(kInvSqrt2Pi * 0x1p-16);
 }
 
+// Phi(x) and phi(x) in fp64 for fp32 data, by the same substitution as
+// norm_cdf with the fp64 table (Q to 4.6e-10 relative), exp_neg and the
+// reciprocal above: Phi within about 5e-10 relative (8e-10 with the forward's
+// shorter exp), phi within a few fp64 ulps for the backward (PRECISE).  The
+// forward x * Phi(x) has no cancellation, so one rounding to fp32
+// keeps it well inside 1e-6; the backward's Phi + x phi cancels near its
+// root, where a Taylor expansion in fp64 takes over (taylor_patch_d).  |x| is
+// clamped to 64, beyond which Phi(-|x|) and phi are 0 in fp64; NaN goes to
+// the clamp too and stays NaN through the products with x.
+template <bool PRECISE> __device__ inline void norm_cdf_d(double x, double &Phi, double &phi)
+{
+    constexpr double cq[GLU_ERFC_QD_DEG + 1] = GLU_ERFC_QD_COEFFS;
+    const double ax = fabs_(x) < 64.0 ? fabs_(x) : 64.0;
+    const double t = recip_ge1(__builtin_fma(ax, 0.5 * kInvSqrt2, 1.0));
+    double q = cq[GLU_ERFC_QD_DEG];
+#pragma unroll
+    for (int k = GLU_ERFC_QD_DEG - 1; k >= 0; --k)
+        q = __builtin_fma(q, t, cq[k]);
+    const double E = exp_neg<PRECISE>(0.5 * ax * ax);
+    const double h = 0.5 * t * q * E;
+    Phi = x >= 0.0 ? 1.0 - h : h;
+    phi = E * kInvSqrt2Pi;
+}
+
+// GELU-erf's derivative near its root for fp32 data (fp64; see gen_taylor.py):
+// inside |x - x0| < 1/32 the expansion, good to 1.5e-13 relative, replaces
+// Phi + x phi, whose table error (5e-10 of Phi ~ 0.23) would otherwise be
+// magnified by the cancellation; outside, that error stays below 1e-8
+// relative.
+__device__ inline double taylor_patch_d(double x, double d)
+{
+    constexpr double c[GLU_TAYLOR_GELU_ERF_D_DEG] = GLU_TAYLOR_GELU_ERF_D_COEFFS;
+    const double h = x - GLU_TAYLOR_GELU_ERF_D_X0_HI;   // exact inside the zone
+    const double t = h - GLU_TAYLOR_GELU_ERF_D_X0_LO;
+    double p = c[GLU_TAYLOR_GELU_ERF_D_DEG - 1];
+#pragma unroll
+    for (int k = GLU_TAYLOR_GELU_ERF_D_DEG - 2; k >= 0; --k)
+        p = __builtin_fma(p, t, c[k]);
+    return __builtin_fabs(h) < 1.0 / 32.0 ? p * t : d;
+}
+
 // Clamp for the tanh form's polynomial: beyond |x| = 16 its sigmoid is 0 or
 // 1 in fp32 (and its contribution below any fp32/bf16/fp16 subnormal), while
 // x^3 would overflow.  NaN passes through.
@@ -121,7 +191,7 @@ template <int KIND, typename M> __device__ inline M act(M x)
 {
     if constexpr (KIND == SILU) {
         // silu(x) = x * sigmoid(x): [SWIGLU] reasoning step 5; [LIGER] Forward Pass
-        const auto sp = sig_parts(fabs_(x));
+        const auto sp = sig_parts<false>(fabs_(x));
         return x * (sp.q * (x >= M(0) ? M(1) : sp.e));
     } else if constexpr (KIND == GELU_ERF) {
         // x * Phi(x), Phi(x) = (1 + erf(x/sqrt2))/2 = erfc(-x/sqrt2)/2: reasoning step 7
@@ -130,13 +200,15 @@ template <int KIND, typename M> __device__ inline M act(M x)
             norm_cdf<false>(x, Phi, phi);
             return x * Phi;
         } else {
-            return x * (M(0.5) * erfc_<M>(x * M(-kInvSqrt2)));
+            double Phi, phi;
+            norm_cdf_d<false>(x, Phi, phi);
+            return x * Phi;
         }
     } else if constexpr (KIND == GELU_TANH) {
         // 0.5*x*(1+tanh(u)) = x * sigmoid(2u), u = sqrt(2/pi)(x + 0.044715 x^3)
         M xc = tanh_clamp(x);
         M w = xc * fma_(M(2 * kSqrt2OverPi * kTanhCubic), xc * xc, M(2 * kSqrt2OverPi));
-        const auto sp = sig_parts(fabs_(w));
+        const auto sp = sig_parts<false>(fabs_(w));
         return x * (sp.q * (w >= M(0) ? M(1) : sp.e));
     } else {
         // relu, NaN-propagating: [SWIGLU] Purpose (ReGLU)
@@ -191,14 +263,14 @@ template <int KIND, bool PATCH, typename M> __device__ inline void act_grad(M x,
     } else if constexpr (KIND == GELU_ERF) {
         // d/dx [x Phi(x)] = Phi(x) + x phi(x)
         M Phi, phi;
-        if constexpr (sizeof(M) == 4) {
+        if constexpr (sizeof(M) == 4)
             norm_cdf(x, Phi, phi);
-        } else {
-            Phi = M(0.5) * erfc_<M>(x * M(-kInvSqrt2));
-            phi = ex<M>(M(-0.5) * x * x) * M(kInvSqrt2Pi);
-        }
+        else
+            norm_cdf_d<true>(x, Phi, phi);
         f = x * Phi;
         g = fma_(x, phi, Phi);
+        if constexpr (sizeof(M) == 8)
+            g = taylor_patch_d(x, g);
     } else if constexpr (KIND == GELU_TANH) {
         // w = 2u, v = 2x u'; sigmoid(w) (1 + v sigmoid(-w)):
         //   w >= 0:  q^2 * ((1+e) + v*e)

@@ -215,6 +215,40 @@ def test_fp32_wide_range(glu, kind):
     check(db, rdb, f"fp32 {kind} db", exact)
 
 
+@pytest.mark.parametrize("kind", KINDS)
+def test_fp32_dense_sweep(glu, kind):
+    """fp32 data is computed in fp64 with a short exp, reciprocal and (GELU-erf
+    forward) normal-CDF table: a dense sweep of a over [-120, 120], where the
+    results run from overflow-free growth down through the fp32 subnormals to
+    zero, against the oracle within 1e-6 relative."""
+    n = 1 << 20
+    a = torch.linspace(-120.0, 120.0, n, dtype=torch.float64).float()
+    # every fp32 value in windows where an exp argument crosses a range edge
+    # or the result turns subnormal (silu near -87 .. -104, GELU-erf near -13 .. -14.5)
+    wins = [torch.arange(v, v + 4096, dtype=torch.int32).view(torch.float32)
+            for v in (int(np.float32(-87.3).view(np.int32)), int(np.float32(-103.9).view(np.int32)),
+                      int(np.float32(-13.2).view(np.int32)), int(np.float32(-14.1).view(np.int32)),
+                      int(np.float32(0.5).view(np.int32)))]
+    # every fp32 value within 2048 ulps of each act' root, and across the
+    # edge of the GELU-erf root's Taylor zone (|x - x0| = 1/32)
+    for root in (-1.2784645, -0.7517915, -0.7524614, -0.7517915 - 1 / 32, -0.7517915 + 1 / 32):
+        c = int(np.float32(root).view(np.int32))
+        wins.append(torch.arange(c - 2048, c + 2048, dtype=torch.int32).view(torch.float32))
+    a = torch.cat([a] + wins)
+    a = a[: (a.numel() // 512) * 512].reshape(-1, 512)
+    g = torch.Generator().manual_seed(11)
+    for label, b, dy in [("b=dy=1", torch.ones_like(a), torch.ones_like(a)),
+                         ("random b, dy", torch.randn(a.shape, generator=g), torch.randn(a.shape, generator=g))]:
+        ga, gb, gdy = cuda(a, b, dy)
+        fa, fb, fdy = f64(a), f64(b), f64(dy)
+        exact = kind == "relu"
+        check(glu.glu_fwd(kind, "separate", ga, gb), oracle.fwd(kind, fa, fb), f"fp32 {kind} fwd {label}", exact)
+        da, db = glu.glu_bwd(kind, "separate", ga, gb, gdy, inplace=False)
+        rda, rdb = oracle.bwd(kind, fa, fb, fdy)
+        check(da, rda, f"fp32 {kind} da {label}", exact)
+        check(db, rdb, f"fp32 {kind} db {label}", exact)
+
+
 # ---------------------------------------------------------------------------
 # Shapes, strides, alignment, aliasing and canaries
 # ---------------------------------------------------------------------------
