@@ -136,6 +136,24 @@ def cpu_baseline(a, b, dy, bwd_only=False):
     }
 
 
+def event_ms(torch, stream, fn, n, warmup=0):
+    """Average milliseconds per call of fn(0) .. fn(n - 1), launched back to
+    back and bracketed by HIP events recorded on `stream`, the stream the
+    library launches on (torch.cuda.Event on another stream would not see
+    them); `warmup` untimed calls go first."""
+    for i in range(warmup):
+        fn(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def copy_reference(torch, dev, stream):
     """GB/s of torch's plain device copy (one read + one write) of 3/2 of a
     bf16 (4096, 14336) operand pair; also the reference kernel the HBM
@@ -144,16 +162,8 @@ def copy_reference(torch, dev, stream):
     dsts = [torch.empty_like(src) for _ in range(3)]
     for d in dsts:
         d.copy_(src)
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    c0.record(stream)
-    reps = 30
-    for r in range(reps):
-        dsts[r % 3].copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() / (c0.elapsed_time(c1) / reps * 1e-3) / 1e9
+    ms = event_ms(torch, stream, lambda r: dsts[r % 3].copy_(src), 30)
+    copy_gbs = 2 * src.numel() / (ms * 1e-3) / 1e9
     del src, dsts
     torch.cuda.empty_cache()
     return round(copy_gbs, 1)
@@ -225,16 +235,8 @@ def main():
     torch.cuda.synchronize()
 
     def timed(fn, n):
-        """n launches of fn(i) bracketed by HIP events on the launch stream."""
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
+        """Total milliseconds of n launches of fn(i), back to back."""
+        return event_ms(torch, stream, fn, n) * n
 
     # Headline: K whole steps, nothing between the launches.
     torch.cuda.synchronize()
@@ -384,15 +386,7 @@ def bench_providers(args, torch, glu, inputs, dev):
     reps = min(args.steps, 200)
 
     def timed(fn, n):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+        return event_ms(torch, stream, fn, n)
 
     rows_out = []
     compile_error = None
@@ -516,36 +510,18 @@ def bench_add_rmsnorm(args, torch, glu, inputs, dev):
         x, r, h, y = sets[i % nsets]
         glu.glu_add_rmsnorm_fwd(x, r, gamma, 1e-6, h=h, y=y)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = event_ms(torch, stream, step, args.steps, warmup=args.warmup)
     value = step_bytes / (ms * 1e-3) / 1e9
 
     eager = None
     if args.torch_eager:
         import torch.nn.functional as F
         reps = min(args.steps, 100)
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        for i in range(5):   # first calls pay one-time costs
-            F.rms_norm(sets[i % nsets][0] + sets[i % nsets][1], (H,), weight=gamma, eps=1e-6)
-        torch.cuda.synchronize()
-        c0.record(stream)
-        for i in range(reps):
+        def eager_step(i):
             x, r, h, y = sets[i % nsets]
-            hh = x + r
-            F.rms_norm(hh, (H,), weight=gamma, eps=1e-6)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        te = c0.elapsed_time(c1) / reps
+            F.rms_norm(x + r, (H,), weight=gamma, eps=1e-6)
+
+        te = event_ms(torch, stream, eager_step, reps, warmup=5)   # first calls pay one-time costs
         eager = {"us": round(1e3 * te, 2), "GBps": round(step_bytes / (te * 1e-3) / 1e9, 1),
                  "speedup": round(te / ms, 2), "note": "x + residual, then F.rms_norm, bf16; algorithmic bytes / time"}
 
@@ -606,17 +582,7 @@ def bench_strided(args, torch, glu, inputs, dev):
     stream = torch.cuda.current_stream(dev)
 
     def timed(fn, n):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        for i in range(min(n, args.warmup)):
-            fn(i)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+        return event_ms(torch, stream, fn, n, warmup=min(n, args.warmup))
 
     def bwd_dyT(i):
         a, b, dyT, yT = sets[i % len(sets)]
@@ -697,17 +663,7 @@ def bench_gemm(args, torch, glu, inputs, dev):
     steps = min(args.steps, 200)
 
     def timed(fn, n):
-        for i in range(min(n, 10)):
-            fn(i)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+        return event_ms(torch, stream, fn, n, warmup=min(n, 10))
 
     def fused(i):
         x, w, h = sets[i % nsets]
