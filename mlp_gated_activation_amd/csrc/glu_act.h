@@ -62,8 +62,8 @@ template <bool PRECISE = true> __device__ inline SigParts sig_parts(float a)
 // 3e-16 relative, so e carries a few fp64 ulps of error like a library exp,
 // and the sums that cancel near act''s root, (1 + e) + x and its tanh form,
 // stay as accurate as in exact arithmetic to within fp32 rounding.
-// Otherwise (the forwards, whose products do not cancel): degree 8, below
-// |r|^9/9! * e^|r| < 3e-10 relative, far inside fp32's 2^-24.
+// Otherwise (the forwards, whose products do not cancel): degree 7, below
+// |r|^8/8! * e^|r| < 8e-9 relative, far inside fp32's 2^-24.
 // a >= 0 is clamped to 1100, where exp(-a) is already 0 in fp64; NaN also
 // goes to the clamp, so callers keep NaN through their product with x.
 template <bool PRECISE> __device__ inline double exp_neg(double a)
@@ -76,7 +76,7 @@ template <bool PRECISE> __device__ inline double exp_neg(double a)
     r = __builtin_fma(k, -kLn2Lo, r);
     constexpr double c[13] = {1.0, 1.0, 1.0 / 2, 1.0 / 6, 1.0 / 24, 1.0 / 120, 1.0 / 720, 1.0 / 5040,
                               1.0 / 40320, 1.0 / 362880, 1.0 / 3628800, 1.0 / 39916800, 1.0 / 479001600};
-    constexpr int deg = PRECISE ? 12 : 8;
+    constexpr int deg = PRECISE ? 12 : 7;
     double p = c[deg];
 #pragma unroll
     for (int i = deg - 1; i >= 0; --i)
@@ -139,23 +139,26 @@ template <bool PRECISE = true> __device__ inline void norm_cdf(float x, float &P
 }
 
 // Phi(x) and phi(x) in fp64 for fp32 data, by the same substitution as
-// norm_cdf with the fp64 table (Q to 4.6e-10 relative), exp_neg and the
-// reciprocal above: Phi within about 5e-10 relative (8e-10 with the forward's
-// shorter exp), phi within a few fp64 ulps for the backward (PRECISE).  The
-// forward x * Phi(x) has no cancellation, so one rounding to fp32
+// norm_cdf with fp64 tables, exp_neg and the reciprocal above.  PRECISE (the
+// backward): Q to 4.6e-10 relative, so Phi within about 5e-10 and phi within
+// a few fp64 ulps.  Otherwise (the forward): Q to 1.2e-8 and the shorter exp,
+// Phi within about 2e-8.  The forward x * Phi(x) has no cancellation, so
+// one rounding to fp32
 // keeps it well inside 1e-6; the backward's Phi + x phi cancels near its
 // root, where a Taylor expansion in fp64 takes over (taylor_patch_d).  |x| is
 // clamped to 64, beyond which Phi(-|x|) and phi are 0 in fp64; NaN goes to
 // the clamp too and stays NaN through the products with x.
 template <bool PRECISE> __device__ inline void norm_cdf_d(double x, double &Phi, double &phi)
 {
-    constexpr double cq[GLU_ERFC_QD_DEG + 1] = GLU_ERFC_QD_COEFFS;
+    constexpr int deg = PRECISE ? GLU_ERFC_QD_DEG : GLU_ERFC_QDF_DEG;
+    constexpr double cp[GLU_ERFC_QD_DEG + 1] = GLU_ERFC_QD_COEFFS;
+    constexpr double cf[GLU_ERFC_QDF_DEG + 1] = GLU_ERFC_QDF_COEFFS;
     const double ax = fabs_(x) < 64.0 ? fabs_(x) : 64.0;
     const double t = recip_ge1(__builtin_fma(ax, 0.5 * kInvSqrt2, 1.0));
-    double q = cq[GLU_ERFC_QD_DEG];
+    double q = PRECISE ? cp[deg] : cf[deg];
 #pragma unroll
-    for (int k = GLU_ERFC_QD_DEG - 1; k >= 0; --k)
-        q = __builtin_fma(q, t, cq[k]);
+    for (int k = deg - 1; k >= 0; --k)
+        q = __builtin_fma(q, t, PRECISE ? cp[k] : cf[k]);
     const double E = exp_neg<PRECISE>(0.5 * ax * ax);
     const double h = 0.5 * t * q * E;
     Phi = x >= 0.0 ? 1.0 - h : h;
