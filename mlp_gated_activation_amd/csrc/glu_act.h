@@ -118,7 +118,8 @@ constexpr double kTanhCubic = 0.044715;
 // Otherwise (the forward x Phi(x)): the degree-5 table, Q to 6.5e-5, i.e.
 // at most about 0.13 fp16 ulp of the result before its rounding.
 constexpr float kLog2e = 1.44269504088896341f;
-template <bool PRECISE = true> __device__ inline void norm_cdf(float x, float &Phi, float &phi)
+// norm_tail returns h = Phi(-|x|) and Es; norm_cdf turns them into Phi, phi.
+template <bool PRECISE> __device__ inline float norm_tail(float x, float &Es)
 {
     constexpr int deg = PRECISE ? GLU_ERFC_Q_DEG : GLU_ERFC_QF_DEG;
     constexpr float cp[GLU_ERFC_Q_DEG + 1] = GLU_ERFC_Q_COEFFS;
@@ -132,35 +133,50 @@ template <bool PRECISE = true> __device__ inline void norm_cdf(float x, float &P
 #pragma unroll
     for (int k = deg - 1; k >= 0; --k)
         q = fma_(q, t, (PRECISE ? cp[k] : cf[k]) * kS);
-    const float Es = __builtin_amdgcn_exp2f(fma_(x * x, -0.5f * kLog2e, 16.0f));
-    const float h = (t * q) * Es;
+    Es = __builtin_amdgcn_exp2f(fma_(x * x, -0.5f * kLog2e, 16.0f));
+    return (t * q) * Es;
+}
+template <bool PRECISE = true> __device__ inline void norm_cdf(float x, float &Phi, float &phi)
+{
+    float Es;
+    const float h = norm_tail<PRECISE>(x, Es);
     Phi = x >= 0.0f ? 1.0f - h : h;
     phi = Es * float(kInvSqrt2Pi * 0x1p-16);
 }
+// x * Phi(x) = relu(x) - |x| h for either sign (Phi = 1 - h for x >= 0, h
+// below): one fma, so one rounding instead of two, and no select.  |x| is
+// clamped to 64, past which h is 0, so +inf gives +inf rather than inf * 0;
+// NaN stays NaN through h.
+__device__ inline float x_phi(float x, float h) { return fma_(-__builtin_fminf(fabs_(x), 64.0f), h, __builtin_fmaxf(x, 0.0f)); }
+__device__ inline double x_phi(double x, double h) { return fma_(-__builtin_fmin(fabs_(x), 64.0), h, __builtin_fmax(x, 0.0)); }
 
 // Phi(x) and phi(x) in fp64 for fp32 data, by the same substitution as
 // norm_cdf with fp64 tables, exp_neg and the reciprocal above.  PRECISE (the
 // backward): Q to 4.6e-10 relative, so Phi within about 5e-10 and phi within
 // a few fp64 ulps.  Otherwise (the forward): Q to 1.2e-8 and the shorter exp,
 // Phi within about 2e-8.  The forward x * Phi(x) has no cancellation, so
-// one rounding to fp32
-// keeps it well inside 1e-6; the backward's Phi + x phi cancels near its
+// one rounding to fp32 keeps it well inside 1e-6; the backward's Phi + x phi cancels near its
 // root, where a Taylor expansion in fp64 takes over (taylor_patch_d).  |x| is
-// clamped to 64, beyond which Phi(-|x|) and phi are 0 in fp64; NaN goes to
-// the clamp too and stays NaN through the products with x.
-template <bool PRECISE> __device__ inline void norm_cdf_d(double x, double &Phi, double &phi)
+// clamped to 64, beyond which Phi(-|x|) and phi are 0 in fp64; NaN passes
+// the clamp and makes h NaN.
+template <bool PRECISE> __device__ inline double norm_tail_d(double x, double &E)
 {
     constexpr int deg = PRECISE ? GLU_ERFC_QD_DEG : GLU_ERFC_QDF_DEG;
     constexpr double cp[GLU_ERFC_QD_DEG + 1] = GLU_ERFC_QD_COEFFS;
     constexpr double cf[GLU_ERFC_QDF_DEG + 1] = GLU_ERFC_QDF_COEFFS;
-    const double ax = fabs_(x) < 64.0 ? fabs_(x) : 64.0;
+    const double ax = fabs_(x) > 64.0 ? 64.0 : fabs_(x);
     const double t = recip_ge1(__builtin_fma(ax, 0.5 * kInvSqrt2, 1.0));
     double q = PRECISE ? cp[deg] : cf[deg];
 #pragma unroll
     for (int k = deg - 1; k >= 0; --k)
         q = __builtin_fma(q, t, PRECISE ? cp[k] : cf[k]);
-    const double E = exp_neg<PRECISE>(0.5 * ax * ax);
-    const double h = 0.5 * t * q * E;
+    E = exp_neg<PRECISE>(0.5 * ax * ax);
+    return 0.5 * t * q * E;
+}
+template <bool PRECISE> __device__ inline void norm_cdf_d(double x, double &Phi, double &phi)
+{
+    double E;
+    const double h = norm_tail_d<PRECISE>(x, E);
     Phi = x >= 0.0 ? 1.0 - h : h;
     phi = E * kInvSqrt2Pi;
 }
@@ -198,15 +214,11 @@ template <int KIND, typename M> __device__ inline M act(M x)
         return x * (sp.q * (x >= M(0) ? M(1) : sp.e));
     } else if constexpr (KIND == GELU_ERF) {
         // x * Phi(x), Phi(x) = (1 + erf(x/sqrt2))/2 = erfc(-x/sqrt2)/2: reasoning step 7
-        if constexpr (sizeof(M) == 4) {
-            float Phi, phi;
-            norm_cdf<false>(x, Phi, phi);
-            return x * Phi;
-        } else {
-            double Phi, phi;
-            norm_cdf_d<false>(x, Phi, phi);
-            return x * Phi;
-        }
+        M E;
+        if constexpr (sizeof(M) == 4)
+            return x_phi(x, norm_tail<false>(x, E));
+        else
+            return x_phi(x, norm_tail_d<false>(x, E));
     } else if constexpr (KIND == GELU_TANH) {
         // 0.5*x*(1+tanh(u)) = x * sigmoid(2u), u = sqrt(2/pi)(x + 0.044715 x^3)
         M xc = tanh_clamp(x);
