@@ -639,8 +639,6 @@ def bench_strided(args, torch, glu, inputs, dev):
             "copy_then_bwd": {"avg_us": round(1e3 * t_copy, 2), "GBps": gbs(BWD_BYTES, t_copy),
                               "path": "dy.contiguous() + row-major backward"},
         },
-        "warm": {"ms_per_step": round(warm_ms, 5), "GBps": round(STEP_BYTES / (warm_ms * 1e-3) / 1e9, 1),
-                 "note": "the same buffer set every step"},
         "torch_copy_GBps": copy,
         "roofline": {"bound": "hbm", "kernel": "glu_tile_kernel<bf16, silu, bwd>", "achieved": value,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4),
@@ -720,8 +718,6 @@ def bench_gemm(args, torch, glu, inputs, dev):
                                        "note": "the unfused path: GEMM writes [g | u], glu_fwd reads it"},
         },
         "speedup_vs_unfused": round(t_unfused / t_fused, 3),
-        "warm": {"ms_per_step": round(warm_ms, 5), "GBps": round(STEP_BYTES / (warm_ms * 1e-3) / 1e9, 1),
-                 "note": "the same buffer set every step"},
         "torch_copy_GBps": copy,
         "roofline": {"bound": "mfma", "kernel": "gemm_glu_kernel<bf16, silu>", "achieved": value,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
