@@ -521,8 +521,15 @@ hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args
     // CU the forward falls back.  The GELU backwards, with more arithmetic per
     // element, lost 4 % capped (fp16 [gate | up] 8191 x 18944), and fp32 data
     // (fp64 arithmetic) lost up to 8 %: those keep every workgroup they can.
+    // Small launches, too: below 2^22 units (4096 x 8192 bf16) the cap leaves
+    // a second, partial round of workgroups, and uncapped they ran 2-3.5 %
+    // faster at 4096 x 512 .. 3072 (even at 4096 x 4096 .. 6144), while the
+    // cap gained 1 % from 4096 x 8192 up.
     constexpr unsigned kFwdLds = 6400, kBwdLds = 16384;
-    const bool cap = dtype != F32 && (kind == SILU || kind == RELU);
+#ifndef GLU_CAP_MIN_UNITS
+#define GLU_CAP_MIN_UNITS (1u << 22)
+#endif
+    const bool cap = dtype != F32 && (kind == SILU || kind == RELU) && args.units >= uint32_t(GLU_CAP_MIN_UNITS);
     const unsigned lds = !cap ? 0u : backward ? kBwdLds : kFwdLds;
     return hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block, kargs, lds, stream);
 }
