@@ -33,6 +33,10 @@ import torch.nn as nn
 from . import glu as _glu
 
 _KINDS = ("silu", "gelu_erf", "gelu_tanh", "relu")
+# Hugging Face activation names (a config's hidden_act) -> kinds: "gelu" is
+# the exact erf form; "gelu_new" and "gelu_pytorch_tanh" are the tanh form.
+HF_ACTIVATIONS = {"silu": "silu", "swish": "silu", "gelu": "gelu_erf", "gelu_new": "gelu_tanh",
+                  "gelu_pytorch_tanh": "gelu_tanh", "relu": "relu"}
 
 
 def _row_major(t: torch.Tensor) -> bool:
@@ -237,6 +241,30 @@ class GatedMLP(nn.Module):
             self.gate_proj = nn.Linear(hidden_size, intermediate_size, **kw)
             self.up_proj = nn.Linear(hidden_size, intermediate_size, **kw)
         self.down_proj = nn.Linear(intermediate_size, hidden_size, **kw)
+
+    @classmethod
+    def from_config(cls, config, **kwargs) -> "GatedMLP":
+        """Build from a Hugging Face model config ("Kernel Profile: SwiGLU",
+        Module Parameters: the module takes the model config): its
+        hidden_size, intermediate_size and hidden_act, which must be one of
+        HF_ACTIVATIONS.  A config with mlp_bias set is refused (the
+        projections here have no bias).  kwargs go to the constructor."""
+        act = getattr(config, "hidden_act", "silu")
+        if act not in HF_ACTIVATIONS:
+            raise ValueError(f"hidden_act {act!r} is not a gated activation this module computes; "
+                             f"expected one of {sorted(HF_ACTIVATIONS)}")
+        if getattr(config, "mlp_bias", False):
+            raise ValueError("mlp_bias=True: the gate, up and down projections here have no bias")
+        return cls(config.hidden_size, config.intermediate_size, HF_ACTIVATIONS[act], **kwargs)
+
+    def _load_from_state_dict(self, state_dict, prefix, *args, **kwargs):
+        # A state dict with separate gate and up weights (the Hugging Face
+        # layout, gate_proj / up_proj / down_proj) loads into the fused
+        # [gate | up] projection: gate rows first, then up rows.
+        g, u = prefix + "gate_proj.weight", prefix + "up_proj.weight"
+        if self.fused_gate_up and g in state_dict and u in state_dict:
+            state_dict[prefix + "gate_up_proj.weight"] = torch.cat([state_dict.pop(g), state_dict.pop(u)], 0)
+        super()._load_from_state_dict(state_dict, prefix, *args, **kwargs)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if self.fused_epilogue:

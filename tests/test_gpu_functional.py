@@ -177,3 +177,42 @@ def test_module_rejects_unknown_kind(fn):
         fn.GatedMLP(8, 8, kind="swish")
     with pytest.raises(ValueError):
         fn.geglu(torch.zeros(1, 8, device="cuda"), torch.zeros(1, 8, device="cuda"), approximate="fast")
+
+
+def _rel_gpu(got, ref):
+    return _rel(got, ref.detach().cpu())
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu", "gelu_pytorch_tanh"])
+@pytest.mark.parametrize("fused", [True, False])
+def test_drop_in_for_hf_llama_mlp(fn, act, fused):
+    """GatedMLP.from_config on a Hugging Face LlamaConfig, loaded with a
+    LlamaMLP's state dict, against that LlamaMLP itself: fp32, (batch, seq,
+    hidden) input, forward and every gradient.  Both sides run the same
+    torch GEMMs; only the activation step differs (here fp64 arithmetic,
+    one rounding), so they agree to fp32 rounding."""
+    transformers = pytest.importorskip("transformers")
+    from transformers.models.llama.modeling_llama import LlamaMLP
+    torch.manual_seed(5)
+    cfg = transformers.LlamaConfig(hidden_size=128, intermediate_size=344, hidden_act=act)
+    ref = LlamaMLP(cfg).to("cuda", torch.float32)
+    mlp = fn.GatedMLP.from_config(cfg, fused_gate_up=fused).to("cuda", torch.float32)
+    mlp.load_state_dict(ref.state_dict())
+    x = torch.randn(3, 37, 128, device="cuda")
+    xr = x.clone().requires_grad_()
+    xm = x.clone().requires_grad_()
+    yr = ref(xr)
+    ym = mlp(xm)
+    dy = torch.randn_like(yr)
+    yr.backward(dy)
+    ym.backward(dy)
+    assert _rel_gpu(ym, yr) < 1e-5
+    assert _rel_gpu(xm.grad, xr.grad) < 1e-5
+    assert _rel_gpu(mlp.down_proj.weight.grad, ref.down_proj.weight.grad) < 1e-5
+    if fused:
+        gw = mlp.gate_up_proj.weight.grad
+        assert _rel_gpu(gw[:344], ref.gate_proj.weight.grad) < 1e-5
+        assert _rel_gpu(gw[344:], ref.up_proj.weight.grad) < 1e-5
+    else:
+        assert _rel_gpu(mlp.gate_proj.weight.grad, ref.gate_proj.weight.grad) < 1e-5
+        assert _rel_gpu(mlp.up_proj.weight.grad, ref.up_proj.weight.grad) < 1e-5
