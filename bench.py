@@ -172,13 +172,15 @@ def copy_reference(torch, dev, stream):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=["glu", "add_rmsnorm", "glu_strided", "gemm_glu", "providers"], default="glu",
+    ap.add_argument("--op", choices=["glu", "add_rmsnorm", "glu_strided", "gemm_glu", "providers", "mlp"], default="glu",
                     help="glu: the SwiGLU fwd+bwd step (default); add_rmsnorm: the fused residual "
                          "add + RMSNorm forward, bf16, 4096 rows; glu_strided: the SwiGLU backward "
                          "with a transposed incoming gradient (LDS-tiled kernel) and related layouts; "
                          "gemm_glu: the gate/up projection with the activation fused into its epilogue "
                          "(bf16, 4096 tokens, hidden 4096, I 14336); providers: the SwiGLU op at "
-                         "4096 x H, H = 1024 .. 16384, against torch eager and torch.compile")
+                         "4096 x H, H = 1024 .. 16384, against torch eager and torch.compile; mlp: a whole "
+                         "SwiGLU MLP training step (4096 tokens, 4096 -> 14336, bf16), GatedMLP against the "
+                         "same network in torch, time and peak memory")
     ap.add_argument("--hidden", type=int, default=4096, help="add_rmsnorm only: row width")
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
@@ -218,6 +220,8 @@ def main():
         return bench_gemm(args, torch, glu, inputs, dev)
     if args.op == "providers":
         return bench_providers(args, torch, glu, inputs, dev)
+    if args.op == "mlp":
+        return bench_mlp(args, torch, dev)
     w = inputs.WORKLOADS["swiglu_bf16_4096x14336"]
     a_h, b_h, dy_h = w.make(seed=0)
     sets = []
@@ -496,6 +500,92 @@ def bench_providers(args, torch, glu, inputs, dev):
     }
     if compile_error is not None:
         result["torch_compile_error"] = compile_error
+    print(json.dumps(result), flush=True)
+
+
+def bench_mlp(args, torch, dev):
+    """A whole SwiGLU MLP training step, down(silu(gate(x)) * up(x)) forward
+    and backward, 4096 tokens, hidden 4096, intermediate 14336, bf16:
+    GatedMLP (torch GEMMs around this library's activation kernels, in-place
+    backward) against the same network in plain torch with the same weights,
+    and optionally under torch.compile.  Time per step and the peak memory a
+    step allocates beyond its inputs and weights ("Kernel Profile: SwiGLU",
+    Key Patterns: the in-place backward saves an allocation).  Context for
+    the op-level figures: the GEMMs dominate the step."""
+    import torch.nn.functional as F
+    from mlp_gated_activation_amd.functional import GatedMLP
+    tokens, hidden, inter = 4096, 4096, 14336
+    torch.manual_seed(0)
+    ours = GatedMLP(hidden, inter, device=dev, dtype=torch.bfloat16)
+    wg = ours.gate_up_proj.weight[:inter].detach()
+    wu = ours.gate_up_proj.weight[inter:].detach()
+    wd = ours.down_proj.weight.detach()
+
+    class TorchMLP(torch.nn.Module):
+        def __init__(self):
+            super().__init__()
+            self.gate_proj = torch.nn.Linear(hidden, inter, bias=False, device=dev, dtype=torch.bfloat16)
+            self.up_proj = torch.nn.Linear(hidden, inter, bias=False, device=dev, dtype=torch.bfloat16)
+            self.down_proj = torch.nn.Linear(inter, hidden, bias=False, device=dev, dtype=torch.bfloat16)
+
+        def forward(self, x):
+            return self.down_proj(F.silu(self.gate_proj(x)) * self.up_proj(x))
+
+    ref = TorchMLP()
+    with torch.no_grad():
+        ref.gate_proj.weight.copy_(wg)
+        ref.up_proj.weight.copy_(wu)
+        ref.down_proj.weight.copy_(wd)
+    x = torch.randn(tokens, hidden, device=dev, dtype=torch.bfloat16)
+    dy = torch.randn(tokens, hidden, device=dev, dtype=torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+    steps = min(args.steps, 50)
+
+    def measure(module):
+        params = list(module.parameters())
+
+        def step(i):
+            for q in params:
+                q.grad = None
+            xi = x.detach().requires_grad_()
+            module(xi).backward(dy)
+
+        for i in range(3):
+            step(i)
+        # peak of one step beyond inputs and weights: activations kept for the
+        # backward, temporaries and the weight gradients it allocates
+        for q in params:
+            q.grad = None
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        step(0)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        ms = event_ms(torch, stream, step, steps)
+        return {"ms_per_step": round(ms, 4), "peak_step_MB": round(peak / 2**20, 1)}
+
+    result_ours = measure(ours)
+    result_torch = measure(ref)
+    compiled = None
+    if args.torch_compile:
+        try:
+            compiled = measure(torch.compile(ref))
+        except Exception as e:   # context only
+            compiled = {"error": f"{type(e).__name__}: {e}"[:300]}
+    flops = 3 * 2 * tokens * hidden * inter * 3   # three GEMMs, forward and two per GEMM backward
+    result = {
+        "metric": "SwiGLU MLP training step time, bf16, 4096 tokens, 4096 -> 14336 -> 4096",
+        "value": result_ours["ms_per_step"], "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": 3,
+        "ms_per_step": result_ours["ms_per_step"], "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded randn inputs and gradients; nn.Linear default initialisation)",
+        "config": {"workload": "GatedMLP fwd+bwd vs the same network in torch", "tokens": tokens,
+                   "hidden": hidden, "intermediate": inter, "matmul_TFLOP_per_step": round(flops / 1e12, 3)},
+        "ours": result_ours, "torch": result_torch, "torch_compile": compiled,
+        "speedup_vs_torch": round(result_torch["ms_per_step"] / result_ours["ms_per_step"], 3),
+        "memory_saved_MB": round(result_torch["peak_step_MB"] - result_ours["peak_step_MB"], 1),
+    }
     print(json.dumps(result), flush=True)
 
 
