@@ -104,23 +104,24 @@ def test_k_zero_and_empty(glu):
     assert e.shape == (0, 3)
 
 
-def test_full_size_sampled(glu):
+@pytest.mark.parametrize("kind,dtype", [("silu", "bf16"), ("gelu_erf", "fp16"), ("relu", "bf16")])
+def test_full_size_sampled(glu, kind, dtype):
     """The MLP shape of the benchmark (4096 tokens, hidden 4096, I = 14336),
-    bf16, checked on 64 sampled rows x 256 sampled columns of h and gu."""
+    checked on 64 sampled rows x 256 sampled columns of h and gu."""
     M, N, K = 4096, 14336, 4096
-    x, w = inputs.gemm_glu(M, N, K, "bf16", seed=0)
+    x, w = inputs.gemm_glu(M, N, K, dtype, seed=0)
     gx, gw = x.cuda(), w.cuda()
-    h, gu = glu.glu_gemm_fwd("silu", gx, gw, gu=True)
+    h, gu = glu.glu_gemm_fwd(kind, gx, gw, gu=True)
     torch.cuda.synchronize()
     gen = torch.Generator().manual_seed(1)
     rows = torch.randperm(M, generator=gen)[:64]
     cols = torch.randperm(N, generator=gen)[:256]
     rr, cc = rows.cuda(), cols.cuda()
     hs = h[rr][:, cc]
-    ref, g, u, one = check_h(hs, x[rows], w[:N][cols], w[N:][cols], "silu", "full size")
+    ref, g, u, one = check_h(hs, x[rows], w[:N][cols], w[N:][cols], kind, f"full size {kind} {dtype}")
     for name, got, want, wt in (("g", gu[rr][:, cc], g, w[:N][cols]), ("u", gu[rr][:, cc + N], u, w[N:][cols])):
         err = np.abs(f64(got) - want)
-        assert (err <= pre_bound("bf16", K, f64(x[rows]), f64(wt), want)).all(), f"full-size {name}"
+        assert (err <= pre_bound(dtype, K, f64(x[rows]), f64(wt), want)).all(), f"full-size {kind} {dtype} {name}"
 
 
 def test_rejects(glu):
