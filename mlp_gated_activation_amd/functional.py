@@ -178,6 +178,44 @@ class FusedGateUpActivation(torch.autograd.Function):
         return dx, dw, None
 
 
+class ActDownRecompute(torch.autograd.Function):
+    """out = (act(gu[..., :I]) * gu[..., I:]) @ w_down^T, keeping only gu for
+    the backward: h is recomputed there from gu (one more activation pass)
+    instead of being kept for the down projection's weight gradient, the
+    same trade the kernels make for the sigmoid ("Kernel Profile: SwiGLU",
+    Key Patterns: recomputation over saving).  The backward then runs the
+    elementwise backward in place over gu, as FusedGatedActivation does."""
+
+    @staticmethod
+    def forward(ctx, gu, w_down, kind: str):
+        lead = gu.shape[:-1]
+        gu2 = gu.reshape(-1, gu.shape[-1])
+        if not _row_major(gu2):
+            gu2 = gu2.contiguous()
+        h = _glu.glu_fwd(kind, "gate_up", gu2)
+        out = torch.mm(h, w_down.t())
+        ctx.save_for_backward(gu2, w_down)
+        ctx.kind = kind
+        ctx.lead = lead
+        return out.reshape(*lead, out.shape[-1])
+
+    @staticmethod
+    def backward(ctx, dout):
+        gu2, w_down = ctx.saved_tensors
+        dout2 = dout.reshape(-1, dout.shape[-1])
+        dw = None
+        if ctx.needs_input_grad[1]:
+            h = _glu.glu_fwd(ctx.kind, "gate_up", gu2)
+            dw = torch.mm(dout2.t(), h)
+            del h
+        dgu = None
+        if ctx.needs_input_grad[0]:
+            dh = torch.mm(dout2, w_down)
+            dgu = _glu.glu_bwd(ctx.kind, "gate_up", gu2, None, dh, inplace=True)
+            dgu = dgu.reshape(*ctx.lead, dgu.shape[-1])
+        return dgu, dw, None
+
+
 def gate_up_activation(x: torch.Tensor, w: torch.Tensor, kind: str = "silu") -> torch.Tensor:
     """act(x @ w[:I]^T) * (x @ w[I:]^T) for a fused [gate | up] weight w of
     shape (2I, H), on the matrix cores with the activation in the epilogue."""
@@ -217,6 +255,10 @@ class GatedMLP(nn.Module):
     """down_proj(act(gate_proj(x)) * up_proj(x)) with the activation step on
     the gfx950 kernels.  fused_gate_up=True keeps gate and up as one
     projection of width 2*intermediate_size whose output is [gate | up].
+    recompute_activation=True (with fused_gate_up) keeps only [gate | up]
+    for the backward and recomputes act(gate) * up there (ActDownRecompute),
+    saving one tokens x intermediate_size activation per layer for one more
+    activation pass.
     fused_epilogue=True (needs fused_gate_up, bf16/fp16) computes that
     projection and the activation in one kernel (gate_up_activation).  It is
     off by default: at 4096 x 4096 -> 14336 bf16 the library GEMM followed by
@@ -224,12 +266,15 @@ class GatedMLP(nn.Module):
 
     def __init__(self, hidden_size: int, intermediate_size: int, kind: str = "silu",
                  fused_gate_up: bool = True, inplace_backward: bool = True, fused_epilogue: bool = False,
-                 device=None, dtype=None):
+                 recompute_activation: bool = False, device=None, dtype=None):
         super().__init__()
         if kind not in _KINDS:
             raise ValueError(f"unknown kind {kind!r}")
         if fused_epilogue and not fused_gate_up:
             raise ValueError("fused_epilogue needs fused_gate_up=True")
+        if recompute_activation and (not fused_gate_up or fused_epilogue):
+            raise ValueError("recompute_activation needs fused_gate_up=True and fused_epilogue=False")
+        self.recompute_activation = recompute_activation
         self.kind = kind
         self.fused_gate_up = fused_gate_up
         self.fused_epilogue = fused_epilogue
@@ -269,6 +314,8 @@ class GatedMLP(nn.Module):
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if self.fused_epilogue:
             return self.down_proj(gate_up_activation(x, self.gate_up_proj.weight, self.kind))
+        if self.recompute_activation:
+            return ActDownRecompute.apply(self.gate_up_proj(x), self.down_proj.weight, self.kind)
         if self.fused_gate_up:
             h = gated_activation(self.gate_up_proj(x), None, self.kind, self.inplace_backward)
         else:

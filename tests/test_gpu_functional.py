@@ -216,3 +216,50 @@ def test_drop_in_for_hf_llama_mlp(fn, act, fused):
     else:
         assert _rel_gpu(mlp.gate_proj.weight.grad, ref.gate_proj.weight.grad) < 1e-5
         assert _rel_gpu(mlp.up_proj.weight.grad, ref.up_proj.weight.grad) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("kind", KINDS)
+def test_recompute_activation_matches_and_saves_memory(fn, kind, dtype):
+    """GatedMLP(recompute_activation=True) keeps only [gate | up] and
+    recomputes act(gate) * up in the backward: the same output and gradients
+    as the default module with the same weights (both run the same kernels
+    and torch GEMMs), and a step's peak memory lower by about one
+    tokens x intermediate activation."""
+    torch.manual_seed(3)
+    tokens, hidden, inter = 1024, 256, 2048
+    base = fn.GatedMLP(hidden, inter, kind=kind, device="cuda", dtype=dtype)
+    rec = fn.GatedMLP(hidden, inter, kind=kind, recompute_activation=True, device="cuda", dtype=dtype)
+    rec.load_state_dict(base.state_dict())
+    x = torch.randn(2, tokens // 2, hidden, device="cuda", dtype=dtype)
+    dy = torch.randn(2, tokens // 2, hidden, device="cuda", dtype=dtype)
+
+    def step(m):
+        for q in m.parameters():
+            q.grad = None
+        xi = x.clone().requires_grad_()
+        torch.cuda.synchronize()
+        start = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        out = m(xi)
+        out.backward(dy)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - start
+        return out.detach(), xi.grad, [q.grad for q in m.parameters()], peak
+
+    ob, gxb, gwb, peak_b = step(base)
+    orr, gxr, gwr, peak_r = step(rec)
+    tol = 1e-6 if dtype == torch.float32 else 1e-2
+    assert _rel_gpu(orr, ob) < tol
+    assert _rel_gpu(gxr, gxb) < tol
+    for a, b in zip(gwr, gwb):
+        assert _rel_gpu(a, b) < tol
+    h_bytes = tokens * inter * torch.finfo(dtype).bits // 8
+    assert peak_b - peak_r >= h_bytes // 2, (peak_b, peak_r, h_bytes)
+
+
+def test_recompute_activation_refusals(fn):
+    with pytest.raises(ValueError, match="recompute_activation"):
+        fn.GatedMLP(8, 12, fused_gate_up=False, recompute_activation=True)
+    with pytest.raises(ValueError, match="recompute_activation"):
+        fn.GatedMLP(8, 12, fused_epilogue=True, recompute_activation=True)
