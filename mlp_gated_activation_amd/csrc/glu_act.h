@@ -100,7 +100,6 @@ template <bool PRECISE = true> __device__ inline SigPartsD sig_parts(double a)
     return SigPartsD{e, recip_ge1(1.0 + e)};
 }
 
-
 constexpr double kInvSqrt2 = 0.70710678118654752440;      // [SWIGLU] reasoning step 7
 constexpr double kInvSqrt2Pi = 0.39894228040143267794;
 constexpr double kSqrt2OverPi = 0.79788456080286535588;   // [SWIGLU] failure modes
@@ -147,18 +146,24 @@ template <bool PRECISE = true> __device__ inline void norm_cdf(float x, float &P
 // below): one fma, so one rounding instead of two, and no select.  |x| is
 // clamped to 64, past which h is 0, so +inf gives +inf rather than inf * 0;
 // NaN stays NaN through h.
-__device__ inline float x_phi(float x, float h) { return fma_(-__builtin_fminf(fabs_(x), 64.0f), h, __builtin_fmaxf(x, 0.0f)); }
-__device__ inline double x_phi(double x, double h) { return fma_(-__builtin_fmin(fabs_(x), 64.0), h, __builtin_fmax(x, 0.0)); }
+__device__ inline float x_phi(float x, float h)
+{
+    return fma_(-__builtin_fminf(fabs_(x), 64.0f), h, __builtin_fmaxf(x, 0.0f));
+}
+__device__ inline double x_phi(double x, double h)
+{
+    return fma_(-__builtin_fmin(fabs_(x), 64.0), h, __builtin_fmax(x, 0.0));
+}
 
 // Phi(x) and phi(x) in fp64 for fp32 data, by the same substitution as
 // norm_cdf with fp64 tables, exp_neg and the reciprocal above.  PRECISE (the
 // backward): Q to 4.6e-10 relative, so Phi within about 5e-10 and phi within
 // a few fp64 ulps.  Otherwise (the forward): Q to 1.2e-8 and the shorter exp,
 // Phi within about 2e-8.  The forward x * Phi(x) has no cancellation, so
-// one rounding to fp32 keeps it well inside 1e-6; the backward's Phi + x phi cancels near its
-// root, where a Taylor expansion in fp64 takes over (taylor_patch_d).  |x| is
-// clamped to 64, beyond which Phi(-|x|) and phi are 0 in fp64; NaN passes
-// the clamp and makes h NaN.
+// one rounding to fp32 keeps it well inside 1e-6; the backward's Phi + x phi
+// cancels near its root, where a Taylor expansion in fp64 takes over
+// (taylor_patch_d).  |x| is clamped to 64, beyond which Phi(-|x|) and phi
+// are 0 in fp64; NaN passes the clamp and makes h NaN.
 template <bool PRECISE> __device__ inline double norm_tail_d(double x, double &E)
 {
     constexpr int deg = PRECISE ? GLU_ERFC_QD_DEG : GLU_ERFC_QDF_DEG;
