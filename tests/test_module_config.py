@@ -9,7 +9,10 @@ from types import SimpleNamespace
 import pytest
 import torch
 
-from mlp_gated_activation_amd import functional as F
+from conftest import ensure_built
+
+ensure_built()
+from mlp_gated_activation_amd import functional as F  # noqa: E402
 
 
 @pytest.mark.parametrize("act,kind", [("silu", "silu"), ("swish", "silu"), ("gelu", "gelu_erf"),
