@@ -9,7 +9,9 @@ from __future__ import annotations
 
 import builtins
 import os
+import subprocess
 import symtable
+import sys
 
 import pytest
 
@@ -44,3 +46,10 @@ def test_the_check_sees_a_planted_mistake(tmp_path):
     p = tmp_path / "planted.py"
     p.write_text("X = 1\n\ndef f():\n    y = 2\n    return X + y\n\ndef g():\n    return y_from_f\n")
     assert undefined_globals(str(p)) == ["g: y_from_f"]
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py --gpus 2 stops with a message before touching a GPU."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2 and "one GPU" in r.stderr
