@@ -517,6 +517,11 @@ glu_status glu_fwd(glu_kind kind, glu_layout layout, glu_dtype dtype, int64_t ro
         if (y != nullptr)
             return GLU_ERR_INPLACE;
         ry = rb;   // [SWIGLU] Inputs, item 7: y may overwrite b
+        // a may coincide with b exactly, but a partial overlap would let one
+        // lane's store land on an element another lane still reads as a
+        const Region ins[1] = {ra};
+        if (bad_alias(rows, ry, ins, 1, es))
+            return GLU_ERR_ALIAS;
     } else {
         if (y == nullptr)
             return GLU_ERR_NULL;

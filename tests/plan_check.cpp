@@ -7,6 +7,7 @@
 // the launches tile the rows x cols problem exactly once.
 //
 // usage: plan_check <fwd|bwd> <layout> <dtype> <rows> <cols> <ld_in> <ld_out> <misalign>
+//        plan_check inplace      (exact in-place aliasing is accepted)
 // prints "ok <launches>" or "FAIL <reason>".
 #include "glu.h"
 #include "glu_internal.h"
@@ -47,8 +48,26 @@ static int fail(const char *why, long long a = 0, long long b = 0)
     return 1;
 }
 
+// In-place calls the boundary must accept: a forward whose y := b is exactly
+// a (so a == b), and the [gate | up] forward whose y := b is x's second half.
+static int accepted_inplace()
+{
+    const uintptr_t A = uintptr_t(1) << 44;
+    glu_status st = glu_fwd(GLU_SILU, GLU_SEPARATE, GLU_BF16, 4, 64, (void *)A, 64, (void *)A, 64, nullptr, 64,
+                            1, nullptr);
+    if (st != GLU_OK || glu::g_launches.size() != 1 || glu::g_launches[0].out0 != (void *)A)
+        return fail("a == b in place", st);
+    st = glu_fwd(GLU_SILU, GLU_GATE_UP, GLU_BF16, 4, 64, (void *)A, 128, nullptr, 0, nullptr, 0, 1, nullptr);
+    if (st != GLU_OK || glu::g_launches.size() != 2 || glu::g_launches[1].out0 != (void *)(A + 128))
+        return fail("gate_up in place", st);
+    std::printf("ok %zu\n", glu::g_launches.size());
+    return 0;
+}
+
 int main(int argc, char **argv)
 {
+    if (argc == 2 && std::strcmp(argv[1], "inplace") == 0)
+        return accepted_inplace();
     if (argc != 9)
         return fail("usage");
     const bool bwd = std::strcmp(argv[1], "bwd") == 0;

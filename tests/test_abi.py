@@ -70,6 +70,10 @@ def bwd(kind=0, layout=S, dtype=BF16, rows=4, cols=64, a=P, lda=64, b=P + (1 << 
     (dict(lda=63), STRIDE), (dict(ldb=10), STRIDE), (dict(ldy=0), STRIDE),
     (dict(layout=GU, b=None, lda=127), STRIDE),                  # x needs 2*cols
     (dict(inplace=1), INPLACE),                                  # y given with inplace
+    (dict(inplace=1, y=None, b=P + 2), ALIAS),                   # y := b one element past a
+    (dict(inplace=1, y=None, b=P + 2 * 63), ALIAS),              # y := b over a's last element
+    (dict(inplace=1, y=None, b=P - 2 * 63 - 2 * 64 * 3), ALIAS),  # b's last row ends inside a's first
+    (dict(inplace=1, y=None, b=P, ldb=128), ALIAS),              # same start, other stride
     (dict(rows=1 << 30, lda=1 << 40), SHAPE),                    # extent overflows int64
     (dict(cols=1 << 62, lda=1 << 62, ldb=1 << 62, ldy=1 << 62, rows=2), SHAPE),
     (dict(y=P + 2 * 2), ALIAS),                                  # y straddles a's rows

@@ -50,3 +50,10 @@ CASES = [
 def test_plan(checker, case):
     out = subprocess.run([checker, *map(str, case)], capture_output=True, text=True)
     assert out.stdout.startswith("ok"), out.stdout + out.stderr
+
+
+def test_exact_inplace_alias_accepted(checker):
+    # the alias check rejects partial overlaps (test_abi.py) but must let the
+    # exact in-place cases through to the launch
+    out = subprocess.run([checker, "inplace"], capture_output=True, text=True)
+    assert out.stdout.startswith("ok 2"), out.stdout + out.stderr
