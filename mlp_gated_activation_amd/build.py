@@ -1,4 +1,6 @@
-"""Builds libglu.so (the C-ABI library with the gfx950 kernels) in-tree.
+"""Builds libglu.so (the C-ABI library with the gfx950 kernels) in-tree,
+and libglu_ref.so (the data-movement reference kernels the benchmark
+measures the library against, include/glu_ref.h).
 
     python -m mlp_gated_activation_amd.build [--out PATH] [-DNAME=VALUE ...]
 
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libglu.so")
+REF_LIB = os.path.join(PKG, "libglu_ref.so")
+REF_SOURCES = [os.path.join(CSRC, "stream_ref.hip")]
 SOURCES = [os.path.join(CSRC, "glu_kernels.hip"), os.path.join(CSRC, "rmsnorm_kernels.hip"),
            os.path.join(CSRC, "gemm_kernels.hip"), os.path.join(CSRC, "glu_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,8 +35,15 @@ FLAGS = [
 
 
 def build(out: str = LIB, defines=(), verbose: bool = False) -> str:
+    """Builds libglu.so at `out`, and libglu_ref.so beside the default one."""
+    if out == LIB:
+        _compile(REF_SOURCES, REF_LIB, defines, verbose)
+    return _compile(SOURCES, out, defines, verbose)
+
+
+def _compile(sources, out, defines, verbose):
     cmd = [HIPCC, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *[f"-D{d}" for d in defines],
-           *SOURCES, "-o", out + ".tmp"]
+           *sources, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -525,12 +525,8 @@ hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args
     // a second, partial round of workgroups, and uncapped they ran 2-3.5 %
     // faster at 4096 x 512 .. 3072 (even at 4096 x 4096 .. 6144), while the
     // cap gained 1 % from 4096 x 8192 up.
-    constexpr unsigned kFwdLds = 6400, kBwdLds = 16384;
-#ifndef GLU_CAP_MIN_UNITS
-#define GLU_CAP_MIN_UNITS (1u << 22)
-#endif
-    const bool cap = dtype != F32 && (kind == SILU || kind == RELU) && args.units >= uint32_t(GLU_CAP_MIN_UNITS);
-    const unsigned lds = !cap ? 0u : backward ? kBwdLds : kFwdLds;
+    const bool cap = dtype != F32 && (kind == SILU || kind == RELU) && args.units >= kCapMinUnits;
+    const unsigned lds = !cap ? 0u : backward ? kCapLdsBwd : kCapLdsFwd;
     return hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block, kargs, lds, stream);
 }
 
