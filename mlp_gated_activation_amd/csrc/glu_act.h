@@ -58,6 +58,11 @@ template <bool PRECISE = true> __device__ inline SigParts sig_parts(float a)
 // r = -a - k ln2 reduced in two steps (ln2 = L1 + L2, L1 with 32 significant
 // bits, so k * L1 is exact for the |k| <= 1587 here and the first step is an
 // exact difference), |r| <= ln2/2 + 2^-40; exp(r) by its Taylor polynomial.
+// This is Cody and Waite's additive argument reduction (W. J. Cody and
+// W. Waite, "Software Manual for the Elementary Functions", 1980).  L1 is ln2
+// truncated to 32 significant bits and L2 = ln2 - L1 rounded to fp64: the
+// same two words as the ln2_hi / ln2_lo split of Sun's fdlibm exp (e_exp.c);
+// tests/test_act_tables.py derives both from a 200-bit ln2.
 // PRECISE (the backward): degree 12, truncation below |r|^13/13! * e^|r| <
 // 3e-16 relative, so e carries a few fp64 ulps of error like a library exp,
 // and the sums that cancel near act''s root, (1 + e) + x and its tanh form,

@@ -104,3 +104,18 @@ def test_gelu_erf_fp64_root_patch():
         p = sum(mp.mpf(ck) * d ** (k + 1) for k, ck in enumerate(c))
         worst = max(worst, abs(p / g(x0 + d) - 1))
     assert worst < 1e-11, float(worst)
+
+
+def test_ln2_split_is_the_cody_waite_split():
+    """The two-word ln2 of the fp64 exp's argument reduction: L1 is ln2
+    truncated to 32 significant bits (so k * L1 is exact for |k| < 2^21) and
+    L2 is the rest, rounded to fp64; both derived here from a 200-bit ln2."""
+    import mpmath as mp
+    mp.mp.prec = 200
+    text = open(os.path.join(os.path.dirname(HEADER), "glu_act.h")).read()
+    m = re.search(r"kLn2Hi = ([0-9.e+-]+), kLn2Lo = ([0-9.e+-]+);", text)
+    hi, lo = float(m.group(1)), float(m.group(2))
+    ln2 = mp.log(2)
+    assert hi == float(mp.floor(ln2 * 2 ** 32) / 2 ** 32)
+    assert lo == float(ln2 - mp.mpf(hi))
+    assert np.frexp(hi)[0] * 2 ** 32 == int(np.frexp(hi)[0] * 2 ** 32)   # 32 significant bits

@@ -104,3 +104,25 @@ def test_workload_table():
     w4 = inputs.WORKLOADS["geglu_reglu_fp16_gateup_8191x18944"]
     assert w4.rows == 8191 and w4.cols == 18944 and w4.stress
     assert len([n for n in inputs.WORKLOADS if n.startswith("swiglu_bf16_4096x")]) == 7
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_comparator_sees_a_kind_swap(dtype):
+    """The correctly rounded result of one kind, over every finite 16-bit
+    input, fails the one-ulp comparison against every other kind's exact
+    value on hundreds of elements ("Write a Triton SiLU-Mul (SwiGLU) Kernel",
+    Common failure modes: GELU variant mismatch), while it passes against
+    its own.  The GPU test of the same name relies on this margin."""
+    import oracle
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    fa = inputs.all_bit_patterns(dtype).to(torch.float64).numpy()
+    fa = fa[np.isfinite(fa)]
+    one = np.ones_like(fa)
+    rnd = lambda v: torch.from_numpy(v).to(tdt).to(torch.float64).numpy()   # fp64 -> 16-bit RNE
+    kinds = ("silu", "gelu_erf", "gelu_tanh", "relu")
+    for k in kinds:
+        y = rnd(oracle.fwd(k, fa, one))
+        assert compare(y, oracle.fwd(k, fa, one), dtype).ok
+        for o in kinds:
+            if o != k:
+                assert compare(y, oracle.fwd(o, fa, one), dtype).n_fail >= 300, (k, o)

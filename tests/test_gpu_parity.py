@@ -191,6 +191,37 @@ def test_exhaustive_16bit(glu, dtype, kind):
                 check(got.cpu()[torch.from_numpy(finite)], ref[finite], f"{dtype} {kind} {label} {nm}", True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("kind", KINDS)
+def test_kind_mismatch_is_caught(glu, dtype, kind):
+    """Negative control ("Write a Triton SiLU-Mul (SwiGLU) Kernel", Common
+    failure modes: GELU variant mismatch): the output of each kind, over every
+    finite 16-bit input, must fail the one-ulp comparison against each OTHER
+    kind's oracle, on many elements, forward and backward.  The closest pair,
+    GELU erf against tanh, differs by more than one bf16 ulp on 335 of the
+    65280 finite bf16 inputs; a kernel that computed the wrong variant, or a
+    comparator too loose to see it, fails here."""
+    a = inputs.all_bit_patterns(dtype).reshape(-1)
+    fa = f64(a)
+    finite = np.isfinite(fa)
+    one = torch.ones_like(a)
+    ga, gone = cuda(a, one)
+    y = f64(glu.glu_fwd(kind, "separate", ga, gone))[finite]
+    da, _ = glu.glu_bwd(kind, "separate", ga, gone, gone.clone(), inplace=False)
+    da = f64(da)[finite]
+    fa, f1 = fa[finite], np.ones(int(finite.sum()))
+    assert compare(y, oracle.fwd(kind, fa, f1), dtype).ok
+    for other in KINDS:
+        if other == kind:
+            continue
+        ry = oracle.fwd(other, fa, f1)
+        rda, _ = oracle.bwd(other, fa, f1, f1)
+        for got, ref, nm in ((y, ry, "y"), (da, rda, "da")):
+            rep = compare(got, ref, dtype)
+            assert not rep.ok and rep.n_fail >= 300, \
+                f"{dtype} {kind} output passes as {other} ({nm}): {rep}"
+
+
 @pytest.mark.parametrize("kind", KINDS)
 def test_fp32_wide_range(glu, kind):
     """fp32 inputs from 1e-30 to 1e3 in magnitude, both signs, plus zeros,
