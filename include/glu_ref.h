@@ -44,6 +44,14 @@ GLU_REF_API int glu_ref_fwd_mix(const void *a, const void *b, void *y, uint64_t 
 GLU_REF_API int glu_ref_bwd_mix(const void *a, const void *b, const void *dy, void *da, void *db,
                                 uint64_t bytes, hipStream_t stream);
 
+/* The fused add + RMSNorm forward's traffic: read x and residual, write h
+ * and y (2:2), as a flat stream: 64-thread workgroups, one vector per stream
+ * per thread and a 6400-byte LDS reservation, the fastest shape a sweep of
+ * 64 / 128 / 256 threads and reservations found for this mix at 4096 rows of
+ * 2048 to 8192 bf16 values. */
+GLU_REF_API int glu_ref_rms_mix(const void *x, const void *r, void *h, void *y, uint64_t bytes,
+                                hipStream_t stream);
+
 /* A plain copy (1:1), 256-thread workgroups: the kernel of known traffic the
  * HBM counters are calibrated on. */
 GLU_REF_API int glu_ref_copy(const void *src, void *dst, uint64_t bytes, hipStream_t stream);

@@ -107,9 +107,20 @@ struct RF32 {
     __device__ static void store1(void *p, double y) { *static_cast<float *>(p) = float(y); }
 };
 
+#ifndef GLU_RMS_NT_LOAD
+#define GLU_RMS_NT_LOAD 1
+#endif
+#ifndef GLU_RMS_NT_STORE
+#define GLU_RMS_NT_STORE 1
+#endif
 template <typename T> __device__ inline u32x4 ldv(const void *base, int64_t off)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const char *>(base) + off * T::SIZE));
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(static_cast<const char *>(base) + off * T::SIZE);
+#if GLU_RMS_NT_LOAD
+    return __builtin_nontemporal_load(q);
+#else
+    return *q;
+#endif
 }
 template <typename T> __device__ inline u32x4 ldv_cached(const void *base, int64_t off)
 {
@@ -118,7 +129,12 @@ template <typename T> __device__ inline u32x4 ldv_cached(const void *base, int64
 }
 template <typename T> __device__ inline void stv(void *base, int64_t off, u32x4 v)
 {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(static_cast<char *>(base) + off * T::SIZE));
+    u32x4 *q = reinterpret_cast<u32x4 *>(static_cast<char *>(base) + off * T::SIZE);
+#if GLU_RMS_NT_STORE
+    __builtin_nontemporal_store(v, q);
+#else
+    *q = v;
+#endif
 }
 __device__ inline const void *at(const void *b, int64_t off, int size) { return static_cast<const char *>(b) + off * size; }
 __device__ inline void *at(void *b, int64_t off, int size) { return static_cast<char *>(b) + off * size; }
@@ -239,6 +255,91 @@ __global__ void __launch_bounds__(BLOCK) add_rmsnorm_kernel(const RmsArgs p)
     }
 }
 
+// Several rows per workgroup, software-pipelined: the workgroup walks rows
+// blockIdx.x, blockIdx.x + gridDim.x, ...; gamma is loaded once and kept in
+// registers (packed) for all of them; and the next row's x and residual
+// loads are issued as soon as this row's h is formed, before its reduction
+// and its y stores, so that each wave always has loads in flight while it
+// reduces and stores.  The arithmetic of every row, and the order of its
+// sum, are those of the one-row kernel (same BLOCK and VPT), so the results
+// are bit-identical.  Vector path only, with H a multiple of the vector
+// width (no ragged vector).
+template <typename T, int BLOCK, int VPT>
+__global__ void __launch_bounds__(BLOCK) add_rmsnorm_rows_kernel(const RmsArgs p, uint32_t rows)
+{
+    using M = typename T::M;
+    constexpr int VE = T::VE;
+    constexpr int NW = BLOCK / 64;
+    __shared__ M lds[2][NW];
+    const uint32_t H = p.hidden;
+    uint32_t row = blockIdx.x;
+    const uint32_t step = gridDim.x;
+
+    u32x4 gp[VPT], xp[VPT], rp[VPT];
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+        const uint32_t col = (uint32_t(v) * BLOCK + threadIdx.x) * VE;
+        if (col + VE <= H) {
+            gp[v] = ldv_cached<T>(p.gamma, col);
+            xp[v] = ldv<T>(at(p.x, int64_t(row) * p.ldx, T::SIZE), col);
+            rp[v] = ldv<T>(at(p.res, int64_t(row) * p.ldr, T::SIZE), col);
+        }
+    }
+    for (int parity = 0; row < rows; row += step, parity ^= 1) {
+        void *hr = at(p.h, int64_t(row) * p.ldh, T::SIZE);
+        void *yr = at(p.y, int64_t(row) * p.ldy, T::SIZE);
+        M h[VPT][VE];
+        M ss = M(0);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const uint32_t col = (uint32_t(v) * BLOCK + threadIdx.x) * VE;
+            if (col + VE <= H) {
+                M xv[VE], rv[VE];
+                T::unpack(xp[v], xv);
+                T::unpack(rp[v], rv);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    h[v][e] = xv[e] + rv[e];
+                    ss += h[v][e] * h[v][e];
+                }
+                stv<T>(hr, col, T::pack(h[v]));
+            }
+        }
+        // the next row's loads go out before this row's reduction
+        const uint32_t next = row + step;
+        if (next < rows) {
+            const void *xr = at(p.x, int64_t(next) * p.ldx, T::SIZE);
+            const void *rr = at(p.res, int64_t(next) * p.ldr, T::SIZE);
+#pragma unroll
+            for (int v = 0; v < VPT; ++v) {
+                const uint32_t col = (uint32_t(v) * BLOCK + threadIdx.x) * VE;
+                if (col + VE <= H) {
+                    xp[v] = ldv<T>(xr, col);
+                    rp[v] = ldv<T>(rr, col);
+                }
+            }
+        }
+        // one LDS slot pair per row parity: a wave that runs ahead into the
+        // next row cannot overwrite totals another wave still reads, since it
+        // would first have to pass that row's barrier
+        const M rs = rsqrt_row<M>(block_sum<M, BLOCK>(ss, lds[parity]) / M(H), p.eps);
+        if (p.rstd != nullptr && threadIdx.x == 0)
+            p.rstd[row] = float(rs);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const uint32_t col = (uint32_t(v) * BLOCK + threadIdx.x) * VE;
+            if (col + VE <= H) {
+                M gv[VE], yv[VE];
+                T::unpack(gp[v], gv);
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    yv[e] = h[v][e] * rs * gv[e];
+                stv<T>(yr, col, T::pack(yv));
+            }
+        }
+    }
+}
+
 // Two passes for rows wider than the register capacity: h is recomputed
 // from x and residual in the second pass (the host guarantees h aliases
 // neither of them).  The first pass reads x and residual through the caches
@@ -307,6 +408,24 @@ __global__ void __launch_bounds__(BLOCK) add_rmsnorm_loop_kernel(const RmsArgs p
 }
 
 typedef void (*RmsFn)(const RmsArgs);
+typedef void (*RmsRowsFn)(const RmsArgs, uint32_t);
+
+// Pipelined instances for the single-pass shapes of the default table with
+// at most 4 vectors per thread and 512 threads (the others keep the one-row
+// kernel: holding the next row on top of this one, their fp32-data
+// instances spill, at 8 vectors per thread or under the 128-register limit
+// of 1024-thread workgroups).
+template <typename T> RmsRowsFn pick_rms_rows(RmsShape s)
+{
+    switch (s.block * 16 + s.vpt) {
+    case 64 * 16 + 1: return &add_rmsnorm_rows_kernel<T, 64, 1>;
+    case 64 * 16 + 2: return &add_rmsnorm_rows_kernel<T, 64, 2>;
+    case 64 * 16 + 4: return &add_rmsnorm_rows_kernel<T, 64, 4>;
+    case 256 * 16 + 4: return &add_rmsnorm_rows_kernel<T, 256, 4>;
+    case 512 * 16 + 4: return &add_rmsnorm_rows_kernel<T, 512, 4>;
+    }
+    return nullptr;
+}
 
 template <typename T, bool VEC> RmsFn pick_rms(RmsShape s)
 {
@@ -342,12 +461,25 @@ template <typename T> RmsFn pick_rms_vec(bool vec, RmsShape s)
 hipError_t launch_add_rmsnorm(int dtype, bool vec, RmsShape shape, uint32_t rows, const RmsArgs &args,
                               hipStream_t stream)
 {
+    RmsArgs copy = args;
+    const int ve = dtype == F32 ? 4 : 8;
+    if (shape.rpb > 1 && vec && shape.vpt > 0 && args.hidden % uint32_t(ve) == 0) {
+        RmsRowsFn rf = dtype == F32 ? pick_rms_rows<RF32>(shape)
+                     : dtype == F16 ? pick_rms_rows<RF16>(shape)
+                                    : pick_rms_rows<RBf16>(shape);
+        if (rf != nullptr) {
+            uint32_t nrows = rows;
+            void *rargs[] = {&copy, &nrows};
+            const uint32_t grid = (rows + uint32_t(shape.rpb) - 1) / uint32_t(shape.rpb);
+            return hipLaunchKernel(reinterpret_cast<const void *>(rf), dim3(grid), dim3(shape.block), rargs, 0,
+                                   stream);
+        }
+    }
     RmsFn fn = dtype == F32 ? pick_rms_vec<RF32>(vec, shape)
              : dtype == F16 ? pick_rms_vec<RF16>(vec, shape)
                             : pick_rms_vec<RBf16>(vec, shape);
     if (fn == nullptr)
         return hipErrorInvalidConfiguration;
-    RmsArgs copy = args;
     void *kargs[] = {&copy};
     // The two-pass kernel reserves LDS it does not use, which keeps one row
     // (workgroup) per CU: bf16 4096 x 131072 3789 -> 4949 GB/s together with

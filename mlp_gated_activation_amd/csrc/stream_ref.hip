@@ -1,11 +1,12 @@
 // stream_ref.hip -- data-movement reference kernels (include/glu_ref.h).
 //
-// Measurement infrastructure, not part of the method: each kernel moves the
-// bytes of one streaming gated-activation launch with the same per-thread
-// access (one 16-byte non-temporal vector per stream), the same workgroup
-// size and the same LDS reservation that caps resident workgroups per CU,
-// and replaces the arithmetic by an XOR.  Built into its own library so the
-// method's library exports only the method's entry points.
+// Measurement infrastructure, not part of the method: the mix kernels move
+// the bytes of one streaming gated-activation launch with the same
+// per-thread access (one 16-byte non-temporal vector per stream), the same
+// workgroup size and the same LDS reservation that caps resident workgroups
+// per CU, and replace the arithmetic by an XOR; the RMSNorm mix moves the
+// fused add + RMSNorm forward's bytes as a flat stream.  Built into its own
+// library so the method's library exports only the method's entry points.
 #include "glu_ref.h"
 #include "glu_internal.h"
 
@@ -41,6 +42,17 @@ __global__ void __launch_bounds__(BLOCK) bwd_mix_kernel(const u32x4 *a, const u3
     const u32x4 vd = __builtin_nontemporal_load(d + i);
     __builtin_nontemporal_store(va ^ vd, da + i);
     __builtin_nontemporal_store(vb ^ vd, db + i);
+}
+
+__global__ void __launch_bounds__(64) rms_mix_kernel(const u32x4 *x, const u32x4 *r, u32x4 *h, u32x4 *y, uint32_t n)
+{
+    const uint32_t i = blockIdx.x * 64u + threadIdx.x;
+    if (i >= n)
+        return;
+    const u32x4 vx = __builtin_nontemporal_load(x + i);
+    const u32x4 vr = __builtin_nontemporal_load(r + i);
+    __builtin_nontemporal_store(vx ^ vr, h + i);
+    __builtin_nontemporal_store(vx + vr, y + i);
 }
 
 __global__ void __launch_bounds__(256) copy_kernel(const u32x4 *s, u32x4 *t, uint32_t n)
@@ -92,6 +104,23 @@ GLU_REF_API int glu_ref_bwd_mix(const void *a, const void *b, const void *dy, vo
                            static_cast<const u32x4 *>(a) + v0, static_cast<const u32x4 *>(b) + v0,
                            static_cast<const u32x4 *>(dy) + v0, static_cast<u32x4 *>(da) + v0,
                            static_cast<u32x4 *>(db) + v0, m);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return int(e);
+    }
+    return 0;
+}
+
+GLU_REF_API int glu_ref_rms_mix(const void *x, const void *r, void *h, void *y, uint64_t bytes, hipStream_t stream)
+{
+    if (bad(x) || bad(r) || bad(h) || bad(y) || (bytes & 15u) != 0)
+        return -1;
+    const uint64_t n = bytes / 16;
+    for (uint64_t v0 = 0; v0 < n; v0 += kMaxVecs) {
+        const uint32_t m = uint32_t(n - v0 < kMaxVecs ? n - v0 : kMaxVecs);
+        hipLaunchKernelGGL(rms_mix_kernel, dim3((m + 63) / 64), dim3(64), glu::kCapLdsFwd, stream,
+                           static_cast<const u32x4 *>(x) + v0, static_cast<const u32x4 *>(r) + v0,
+                           static_cast<u32x4 *>(h) + v0, static_cast<u32x4 *>(y) + v0, m);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return int(e);

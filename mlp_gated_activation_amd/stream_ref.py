@@ -17,8 +17,9 @@ _lib = ctypes.CDLL(_LIB_PATH)
 _p, _u64 = ctypes.c_void_p, ctypes.c_uint64
 _lib.glu_ref_fwd_mix.argtypes = [_p, _p, _p, _u64, _p]
 _lib.glu_ref_bwd_mix.argtypes = [_p, _p, _p, _p, _p, _u64, _p]
+_lib.glu_ref_rms_mix.argtypes = [_p, _p, _p, _p, _u64, _p]
 _lib.glu_ref_copy.argtypes = [_p, _p, _u64, _p]
-for _f in (_lib.glu_ref_fwd_mix, _lib.glu_ref_bwd_mix, _lib.glu_ref_copy):
+for _f in (_lib.glu_ref_fwd_mix, _lib.glu_ref_bwd_mix, _lib.glu_ref_rms_mix, _lib.glu_ref_copy):
     _f.restype = ctypes.c_int
 
 
@@ -53,6 +54,12 @@ def bwd_mix(a, b, dy, da, db):
     """Read a, b and dy, write da and db: the backward's bytes and pattern."""
     _go(_lib.glu_ref_bwd_mix(a.data_ptr(), b.data_ptr(), dy.data_ptr(), da.data_ptr(), db.data_ptr(),
                              _nbytes([a, b, dy, da, db]), _raw(a)), "glu_ref_bwd_mix")
+
+
+def rms_mix(x, r, h, y):
+    """Read x and residual, write h and y: the add + RMSNorm forward's bytes."""
+    _go(_lib.glu_ref_rms_mix(x.data_ptr(), r.data_ptr(), h.data_ptr(), y.data_ptr(), _nbytes([x, r, h, y]), _raw(x)),
+        "glu_ref_rms_mix")
 
 
 def copy(src, dst):

@@ -11,7 +11,8 @@ def pytest_configure(config):
 
 
 def ensure_built():
-    """Build libglu.so only if it is not there yet (the tests never rebuild)."""
+    """Build libglu.so and libglu_ref.so only if they are not there yet (the
+    tests never rebuild)."""
     from mlp_gated_activation_amd import build
-    if not os.path.exists(build.LIB):
+    if not os.path.exists(build.LIB) or not os.path.exists(build.REF_LIB):
         build.build()

@@ -42,6 +42,27 @@ def test_header_declarations_are_exported():
     assert exported == set(names), exported
 
 
+def test_reference_library_exports_its_header():
+    """libglu_ref.so (the benchmark's data-movement reference kernels) exports
+    exactly what include/glu_ref.h declares, and rejects bad arguments on the
+    host before any launch."""
+    import ctypes
+    from mlp_gated_activation_amd import build
+    text = open(os.path.join(ROOT, "include", "glu_ref.h")).read()
+    names = set(re.findall(r"GLU_REF_API\s+int\s+(glu_ref_\w+)\s*\(", text))
+    assert names == {"glu_ref_fwd_mix", "glu_ref_bwd_mix", "glu_ref_rms_mix", "glu_ref_copy"}
+    nm = subprocess.run(["nm", "-D", "--defined-only", build.REF_LIB], capture_output=True, text=True,
+                        check=True).stdout
+    assert {l.split()[-1] for l in nm.splitlines() if " T " in l} == names
+    ref = ctypes.CDLL(build.REF_LIB)
+    p, u64 = ctypes.c_void_p, ctypes.c_uint64
+    ref.glu_ref_copy.argtypes = [p, p, u64, p]
+    ref.glu_ref_fwd_mix.argtypes = [p, p, p, u64, p]
+    assert ref.glu_ref_copy(None, P, 16, None) == -1          # NULL
+    assert ref.glu_ref_copy(P + 8, P, 16, None) == -1         # unaligned
+    assert ref.glu_ref_fwd_mix(P, P, P, 24, None) == -1       # not a multiple of 16 bytes
+
+
 def test_version_and_status_strings():
     assert glu.version() >> 16 == 1
     for s in range(9):
@@ -372,7 +393,9 @@ def test_rmsnorm_kernel_isa():
         subprocess.run(cmd, cwd=tmp, check=True, capture_output=True)
         asm = open(os.path.join(tmp, "rmsnorm_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")).read()
     names = re.findall(r"^(_Z\w*rmsnorm\w*kernel\w*):", asm, re.M)
-    assert len(names) == 3 * 2 * 16   # 15 single-pass shapes + the two-pass kernel
+    # per dtype: 15 one-row shapes and the two-pass kernel, vector and element
+    # paths, and 5 pipelined multi-row shapes (vector path only)
+    assert len(names) == 3 * (2 * 16 + 5)
     # register arrays must stay in registers: no private (scratch) memory
     assert re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm) and \
         set(re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)) == {"0"}
@@ -382,5 +405,5 @@ def test_rmsnorm_kernel_isa():
         assert "mfma" not in body and not re.search(r"v_pk_(add|mul|fma)_f32", body), name
         if "RF32" not in name:
             assert not re.search(r"^\s+v_\w+_f64", body, re.M), name
-        if re.search(r"ELb1EEEvNS_7RmsArgsE", name):   # VEC instances
+        if re.search(r"ELb1EEEvNS_7RmsArgsE", name) or "rows_kernel" in name:   # VEC instances
             assert "global_load_dwordx4" in body and "global_store_dwordx4" in body, name

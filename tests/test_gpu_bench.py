@@ -39,8 +39,9 @@ def test_bench_op_prints_its_line(op):
     if op != "mlp":
         roof = out["roofline"]
         assert roof["peak"] > 0 and 0 < roof["frac"] < 1 and roof["bound"] in ("hbm", "mfma")
-    if op in ("glu", "glu_strided"):
+    if op in ("glu", "glu_strided", "add_rmsnorm"):
         # the same-run ceiling from the data-movement reference kernels
         assert 0 < out["pct_of_attainable"] < 120
-        assert 0 < out["attainable"]["bwd_mix"]["GBps"] < 8000
+        attain = out["attainable"]["bwd_mix"]["GBps"] if op != "add_rmsnorm" else out["attainable"]["GBps"]
+        assert 0 < attain < 8000
 

@@ -88,7 +88,7 @@ def test_strided_rows_inplace_and_canaries(glu, dtype):
     update) or over residual, y over x, with sentinels around every output."""
     t = DT[dtype]
     ib = torch.int32 if t == torch.float32 else torch.int16
-    for hidden, rows in ((1000, 9), (4096, 5), (70000, 2)):
+    for hidden, rows in ((1000, 9), (4096, 5), (8192, 6), (70000, 2)):
         x, r, g = inputs.add_rmsnorm(rows, hidden, dtype, seed=7)
         ld = hidden + 24
         for mode in ("separate", "h_over_x", "h_over_res", "y_over_x"):
