@@ -106,6 +106,22 @@ def gemm_glu(M: int, N: int, K: int, dtype: str, w_std: float = 0.02, seed: int 
     return x, w
 
 
+def gemm_glu_exact(M: int, N: int, K: int, dtype: str, seed: int = 0):
+    """Inputs of the gate/up projection whose sums are exact in fp32 in any
+    order: x (M, K) of integers uniform in [-8, 8] and w (2N, K) of integers
+    uniform in [-8, 8] times 2^-8.  Every product is a multiple of 2^-8 of
+    magnitude at most 1/4, so every partial sum over K <= 2^16 terms is a
+    multiple of 2^-8 below 2^14 in magnitude, which fp32 holds exactly.
+    Draw order: ``x = randint(-8, 9, (M, K))``, ``w = randint(-8, 9, (2N, K))``."""
+    if K > (1 << 16):
+        raise ValueError("K above 2^16: partial sums could leave fp32's exact range")
+    g = _gen(seed)
+    t = DTYPES[dtype]
+    x = torch.randint(-8, 9, (M, K), generator=g).to(t)
+    w = (torch.randint(-8, 9, (2 * N, K), generator=g).to(torch.float32) * 2.0 ** -8).to(t)
+    return x, w
+
+
 def all_bit_patterns(dtype: str) -> torch.Tensor:
     """Every 16-bit pattern of a 16-bit dtype, in bit order, as a 1-D tensor."""
     t = DTYPES[dtype]
