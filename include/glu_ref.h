@@ -52,6 +52,19 @@ GLU_REF_API int glu_ref_bwd_mix(const void *a, const void *b, const void *dy, vo
 GLU_REF_API int glu_ref_rms_mix(const void *x, const void *r, void *h, void *y, uint64_t bytes,
                                 hipStream_t stream);
 
+/* The strided kernels' LDS-tiled access pattern, bf16 only: 64 x 64 tiles,
+ * 256 threads, the tiled kernel's launch order, the transposed operand
+ * turned around through LDS, and 48 KiB of LDS per workgroup (three per CU,
+ * the fastest cap for these mixes).  a, b, da, db are row-major (rows, cols)
+ * with row stride cols; dyT and yT are stored transposed, (cols, rows)
+ * row-major.  rows and cols must be positive multiples of 64 (else -1).
+ * The backward's mix reads a, b and dyT and writes da, db (which may be a,
+ * b); the forward's reads a, b and writes yT. */
+GLU_REF_API int glu_ref_tile_bwd_mix(const void *a, const void *b, const void *dyT, void *da, void *db,
+                                     int64_t rows, int64_t cols, hipStream_t stream);
+GLU_REF_API int glu_ref_tile_fwd_mix(const void *a, const void *b, void *yT, int64_t rows, int64_t cols,
+                                     hipStream_t stream);
+
 /* A plain copy (1:1), 256-thread workgroups: the kernel of known traffic the
  * HBM counters are calibrated on. */
 GLU_REF_API int glu_ref_copy(const void *src, void *dst, uint64_t bytes, hipStream_t stream);

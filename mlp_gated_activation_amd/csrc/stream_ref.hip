@@ -5,7 +5,8 @@
 // per-thread access (one 16-byte non-temporal vector per stream), the same
 // workgroup size and the same LDS reservation that caps resident workgroups
 // per CU, and replace the arithmetic by an XOR; the RMSNorm mix moves the
-// fused add + RMSNorm forward's bytes as a flat stream.  Built into its own
+// fused add + RMSNorm forward's bytes as a flat stream; the tiled mixes move
+// the strided kernels' bytes in their 64 x 64 tile pattern.  Built into its own
 // library so the method's library exports only the method's entry points.
 #include "glu_ref.h"
 #include "glu_internal.h"
@@ -53,6 +54,95 @@ __global__ void __launch_bounds__(64) rms_mix_kernel(const u32x4 *x, const u32x4
     const u32x4 vr = __builtin_nontemporal_load(r + i);
     __builtin_nontemporal_store(vx ^ vr, h + i);
     __builtin_nontemporal_store(vx + vr, y + i);
+}
+
+// Tiled mixes: chunk q = tid + 256 j of a 64 x 64 bf16 tile is row-major
+// line q / 8, segment q % 8 (8 elements); the transposed operand's chunk q is
+// column q / 8, rows 8 (q % 8) .. + 7, turned around through LDS as floats.
+constexpr int kT = 64;
+__device__ inline float lo16(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float hi16(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+__device__ inline uint32_t join16(float lo, float hi)
+{
+    return (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xffff0000u);
+}
+
+__global__ void __launch_bounds__(256) tile_bwd_mix_kernel(const uint16_t *a, const uint16_t *b, const uint16_t *dyT,
+                                                           uint16_t *da, uint16_t *db, int64_t rows, int64_t cols,
+                                                           uint32_t tiles_r, uint32_t tiles_c)
+{
+    __shared__ float lds[kT][kT + 1];
+    const glu::TileCoord tc = glu::tile_coord(blockIdx.x, tiles_r, tiles_c);
+    const int64_t r0 = int64_t(tc.r) * kT, c0 = int64_t(tc.c) * kT;
+    u32x4 va[2], vb[2], vd[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = threadIdx.x + 256 * j, line = q / 8, seg = q % 8;
+        va[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a + (r0 + line) * cols + c0 + seg * 8));
+        vb[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b + (r0 + line) * cols + c0 + seg * 8));
+        vd[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(dyT + (c0 + line) * rows + r0 + seg * 8));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = threadIdx.x + 256 * j, line = q / 8, seg = q % 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w = vd[j][e];
+            lds[seg * 8 + 2 * e][line] = lo16(w);
+            lds[seg * 8 + 2 * e + 1][line] = hi16(w);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = threadIdx.x + 256 * j, line = q / 8, seg = q % 8;
+        u32x4 d;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            d[e] = join16(lds[line][seg * 8 + 2 * e], lds[line][seg * 8 + 2 * e + 1]);
+        __builtin_nontemporal_store(va[j] ^ d, reinterpret_cast<u32x4 *>(da + (r0 + line) * cols + c0 + seg * 8));
+        __builtin_nontemporal_store(vb[j] ^ d, reinterpret_cast<u32x4 *>(db + (r0 + line) * cols + c0 + seg * 8));
+    }
+}
+
+__global__ void __launch_bounds__(256) tile_fwd_mix_kernel(const uint16_t *a, const uint16_t *b, uint16_t *yT,
+                                                           int64_t rows, int64_t cols, uint32_t tiles_r,
+                                                           uint32_t tiles_c)
+{
+    __shared__ float lds[kT][kT + 1];
+    const glu::TileCoord tc = glu::tile_coord(blockIdx.x, tiles_r, tiles_c);
+    const int64_t r0 = int64_t(tc.r) * kT, c0 = int64_t(tc.c) * kT;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = threadIdx.x + 256 * j, line = q / 8, seg = q % 8;
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a + (r0 + line) * cols + c0 + seg * 8)) ^
+                        __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b + (r0 + line) * cols + c0 + seg * 8));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w = v[e];
+            lds[line][seg * 8 + 2 * e] = lo16(w);
+            lds[line][seg * 8 + 2 * e + 1] = hi16(w);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = threadIdx.x + 256 * j, line = q / 8, seg = q % 8;
+        u32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            y[e] = join16(lds[seg * 8 + 2 * e][line], lds[seg * 8 + 2 * e + 1][line]);
+        __builtin_nontemporal_store(y, reinterpret_cast<u32x4 *>(yT + (c0 + line) * rows + r0 + seg * 8));
+    }
+}
+
+// 48 KiB per workgroup in all (the static tile plus this), three per CU.
+constexpr unsigned kTileMixDynLds = 48 * 1024 - kT * (kT + 1) * 4;
+
+bool tile_shape_ok(int64_t rows, int64_t cols)
+{
+    return rows > 0 && cols > 0 && rows % kT == 0 && cols % kT == 0 &&
+           (rows / kT) * (cols / kT) <= int64_t(glu::kMaxTilesPerLaunch);
 }
 
 __global__ void __launch_bounds__(256) copy_kernel(const u32x4 *s, u32x4 *t, uint32_t n)
@@ -126,6 +216,31 @@ GLU_REF_API int glu_ref_rms_mix(const void *x, const void *r, void *h, void *y, 
             return int(e);
     }
     return 0;
+}
+
+GLU_REF_API int glu_ref_tile_bwd_mix(const void *a, const void *b, const void *dyT, void *da, void *db, int64_t rows,
+                                     int64_t cols, hipStream_t stream)
+{
+    if (bad(a) || bad(b) || bad(dyT) || bad(da) || bad(db) || !tile_shape_ok(rows, cols))
+        return -1;
+    const uint32_t tr = uint32_t(rows / kT), tcn = uint32_t(cols / kT);
+    hipLaunchKernelGGL(tile_bwd_mix_kernel, dim3(tr * tcn), dim3(256), kTileMixDynLds, stream,
+                       static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b),
+                       static_cast<const uint16_t *>(dyT), static_cast<uint16_t *>(da), static_cast<uint16_t *>(db), rows,
+                       cols, tr, tcn);
+    return int(hipGetLastError());
+}
+
+GLU_REF_API int glu_ref_tile_fwd_mix(const void *a, const void *b, void *yT, int64_t rows, int64_t cols,
+                                     hipStream_t stream)
+{
+    if (bad(a) || bad(b) || bad(yT) || !tile_shape_ok(rows, cols))
+        return -1;
+    const uint32_t tr = uint32_t(rows / kT), tcn = uint32_t(cols / kT);
+    hipLaunchKernelGGL(tile_fwd_mix_kernel, dim3(tr * tcn), dim3(256), kTileMixDynLds, stream,
+                       static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b), static_cast<uint16_t *>(yT),
+                       rows, cols, tr, tcn);
+    return int(hipGetLastError());
 }
 
 GLU_REF_API int glu_ref_copy(const void *src, void *dst, uint64_t bytes, hipStream_t stream)

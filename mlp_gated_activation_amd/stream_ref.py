@@ -19,7 +19,11 @@ _lib.glu_ref_fwd_mix.argtypes = [_p, _p, _p, _u64, _p]
 _lib.glu_ref_bwd_mix.argtypes = [_p, _p, _p, _p, _p, _u64, _p]
 _lib.glu_ref_rms_mix.argtypes = [_p, _p, _p, _p, _u64, _p]
 _lib.glu_ref_copy.argtypes = [_p, _p, _u64, _p]
-for _f in (_lib.glu_ref_fwd_mix, _lib.glu_ref_bwd_mix, _lib.glu_ref_rms_mix, _lib.glu_ref_copy):
+_i64 = ctypes.c_int64
+_lib.glu_ref_tile_bwd_mix.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _p]
+_lib.glu_ref_tile_fwd_mix.argtypes = [_p, _p, _p, _i64, _i64, _p]
+for _f in (_lib.glu_ref_fwd_mix, _lib.glu_ref_bwd_mix, _lib.glu_ref_rms_mix, _lib.glu_ref_copy,
+           _lib.glu_ref_tile_bwd_mix, _lib.glu_ref_tile_fwd_mix):
     _f.restype = ctypes.c_int
 
 
@@ -60,6 +64,31 @@ def rms_mix(x, r, h, y):
     """Read x and residual, write h and y: the add + RMSNorm forward's bytes."""
     _go(_lib.glu_ref_rms_mix(x.data_ptr(), r.data_ptr(), h.data_ptr(), y.data_ptr(), _nbytes([x, r, h, y]), _raw(x)),
         "glu_ref_rms_mix")
+
+
+def _tile_check(rowmajor, transposed):
+    rows, cols = rowmajor[0].shape
+    for t in rowmajor:
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.shape != (rows, cols):
+            raise ValueError("tiled references take contiguous bf16 (rows, cols) row-major operands")
+    if transposed.dtype != torch.bfloat16 or not transposed.is_contiguous() or transposed.shape != (cols, rows):
+        raise ValueError("the transposed operand must be a contiguous bf16 (cols, rows) tensor")
+    return rows, cols
+
+
+def tile_bwd_mix(a, b, dyT, da, db):
+    """The strided backward's bytes in the tiled kernel's pattern: a, b, da,
+    db row-major (rows, cols), dyT stored as (cols, rows)."""
+    rows, cols = _tile_check([a, b, da, db], dyT)
+    _go(_lib.glu_ref_tile_bwd_mix(a.data_ptr(), b.data_ptr(), dyT.data_ptr(), da.data_ptr(), db.data_ptr(), rows, cols,
+                                  _raw(a)), "glu_ref_tile_bwd_mix")
+
+
+def tile_fwd_mix(a, b, yT):
+    """The strided forward's bytes in the tiled kernel's pattern: a, b
+    row-major (rows, cols), yT stored as (cols, rows)."""
+    rows, cols = _tile_check([a, b], yT)
+    _go(_lib.glu_ref_tile_fwd_mix(a.data_ptr(), b.data_ptr(), yT.data_ptr(), rows, cols, _raw(a)), "glu_ref_tile_fwd_mix")
 
 
 def copy(src, dst):

@@ -50,7 +50,8 @@ def test_reference_library_exports_its_header():
     from mlp_gated_activation_amd import build
     text = open(os.path.join(ROOT, "include", "glu_ref.h")).read()
     names = set(re.findall(r"GLU_REF_API\s+int\s+(glu_ref_\w+)\s*\(", text))
-    assert names == {"glu_ref_fwd_mix", "glu_ref_bwd_mix", "glu_ref_rms_mix", "glu_ref_copy"}
+    assert names == {"glu_ref_fwd_mix", "glu_ref_bwd_mix", "glu_ref_rms_mix", "glu_ref_copy", "glu_ref_tile_bwd_mix",
+                     "glu_ref_tile_fwd_mix"}
     nm = subprocess.run(["nm", "-D", "--defined-only", build.REF_LIB], capture_output=True, text=True,
                         check=True).stdout
     assert {l.split()[-1] for l in nm.splitlines() if " T " in l} == names
@@ -61,6 +62,9 @@ def test_reference_library_exports_its_header():
     assert ref.glu_ref_copy(None, P, 16, None) == -1          # NULL
     assert ref.glu_ref_copy(P + 8, P, 16, None) == -1         # unaligned
     assert ref.glu_ref_fwd_mix(P, P, P, 24, None) == -1       # not a multiple of 16 bytes
+    ref.glu_ref_tile_fwd_mix.argtypes = [p, p, p, ctypes.c_int64, ctypes.c_int64, p]
+    assert ref.glu_ref_tile_fwd_mix(P, P, P, 64, 100, None) == -1     # cols not a multiple of 64
+    assert ref.glu_ref_tile_fwd_mix(P, P, P, 0, 64, None) == -1       # empty
 
 
 def test_version_and_status_strings():
