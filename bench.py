@@ -929,7 +929,22 @@ def bench_gemm(args, torch, glu, inputs, dev):
     t_fused_gu = timed(fused_gu, steps)
     t_blas = timed(blas_only, steps)
     t_unfused = timed(blas_then_glu, steps)
-    del sets, gu
+
+    # Context: the same projection over token counts (four weight copies
+    # rotate, so every call streams the weights from HBM).  At few tokens the
+    # kernel takes its small-tile configuration.
+    m_sweep = []
+    ws = [sets[i % nsets][1] for i in range(2)] + [w_h.to(dev) for _ in range(2)]
+    for Ms in (16, 64, 128, 256, 1024):
+        xs = sets[0][0][:Ms]
+        hs = torch.empty(Ms, N, dtype=torch.bfloat16, device=dev)
+        gus = torch.empty(Ms, 2 * N, dtype=torch.bfloat16, device=dev)
+        t_f = timed(lambda i: glu.glu_gemm_fwd("silu", xs, ws[i % 4], h=hs), 100)
+        t_u = timed(lambda i: (torch.matmul(xs, ws[i % 4].t(), out=gus), glu.glu_fwd("silu", "gate_up", gus, y=hs)), 100)
+        m_sweep.append({"M": Ms, "fused_us": round(1e3 * t_f, 1), "unfused_us": round(1e3 * t_u, 1),
+                        "speedup_vs_unfused": round(t_u / t_f, 3),
+                        "weights_GBps_fused": round(2 * N * K * 2 / (t_f * 1e-3) / 1e9, 1)})
+    del sets, gu, ws
     torch.cuda.empty_cache()
     tf = lambda ms: round(flops / (ms * 1e-3) / 1e12, 1)
     value = tf(t_fused)
@@ -953,6 +968,7 @@ def bench_gemm(args, torch, glu, inputs, dev):
                                        "note": "the unfused path: GEMM writes [g | u], glu_fwd reads it"},
         },
         "speedup_vs_unfused": round(t_unfused / t_fused, 3),
+        "m_sweep": m_sweep,
         "roofline": {"bound": "mfma", "kernel": "gemm_glu_kernel<bf16, silu>", "achieved": value,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
                      "traffic": committed_traffic(GEMM_PMC_SUMMARY, "traffic_bytes", GEMM_SOURCES)},

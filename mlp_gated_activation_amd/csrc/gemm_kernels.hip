@@ -8,11 +8,16 @@
 // through HBM).
 //
 // This is a dense contraction, so it runs on the matrix cores:
-//  - a workgroup of 512 threads (8 waves, 4 x 2; two per SIMD, so one
-//    wave's LDS and barrier waits are covered by the other's MFMAs) owns
-//    256 rows of x and 128 columns of h, i.e. 128 gate and 128 up rows of the
-//    weights; each wave holds a 64 x 64 block of g and the same block of u in
-//    8 fp32 accumulators of v_mfma_f32_32x32x16_{bf16,f16};
+//  - for many tokens, a workgroup of 512 threads (8 waves, 4 x 2; two per
+//    SIMD, so one wave's LDS and barrier waits are covered by the other's
+//    MFMAs) owns 256 rows of x and 128 columns of h, i.e. 128 gate and 128 up
+//    rows of the weights; each wave holds a 64 x 64 block of g and the same
+//    block of u in 8 fp32 accumulators of v_mfma_f32_32x32x16_{bf16,f16};
+//  - for few tokens (at most 256), where streaming the weights bounds the
+//    kernel, a workgroup of 256 threads (4 waves, 2 x 2) owns 128 rows of x
+//    and 64 columns of h, so N / 64 workgroups spread the weights over every
+//    CU; each wave holds a 64 x 32 block of g and of u.  Both tiles sum k in
+//    the same order, so their results are bit-identical;
 //  - both operands are k-contiguous (x rows, weight rows), so every MFMA
 //    fragment is one 16-byte LDS read;
 //  - k advances 64 at a time through two LDS stages of 64 KiB; the next
@@ -28,6 +33,8 @@
 //    staged through LDS and written in whole cache lines.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "glu_act.h"
 #include "glu_internal.h"
@@ -63,27 +70,35 @@ template <> struct MfmaOp<_Float16> {
     }
 };
 
-constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int ROWS = BM + 2 * BN;               // x rows, then gate rows, then up rows
-constexpr int ROW_BYTES = BK * 2;               // one row of a stage
-constexpr int CPR = BK / 8;                     // 16-byte chunks per row
-constexpr int RPI = 1024 / ROW_BYTES;           // rows per wave load instruction (1 KiB)
-constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
-constexpr int NST = (128 * 1024) / STAGE_BYTES; // LDS stages (128 KiB in all), all in flight
+// Tile configurations.  Wave w of WAVES works on tokens [TPW (w / WN), +TPW)
+// and features [FPW (w % WN), +FPW) of the workgroup tile, FPW = BN / WN, in
+// (TPW / 32) x (FPW / 32) blocks of g and as many of u.  LDS_BYTES of LDS
+// hold NST stages of (BM + 2 BN) rows x BK.  OCC: workgroups per CU the
+// launch bounds allow.
+template <int BM_, int BN_, int WAVES_, int WN_, int LDS_BYTES_, int OCC_> struct GemmCfg {
+    static constexpr int BM = BM_, BN = BN_, WAVES = WAVES_, WN = WN_, LDS_BYTES = LDS_BYTES_, OCC = OCC_;
+};
 #ifndef GLU_GEMM_WAVES
 #define GLU_GEMM_WAVES 8   // 4 (one wave per SIMD, 128 x 64 per wave) measured 8 % slower
 #endif
-constexpr int WAVES = GLU_GEMM_WAVES;           // (WAVES/2) x 2 waves per workgroup
-constexpr int THREADS = 64 * WAVES;
-constexpr int RPW = ROWS / WAVES;               // stage rows each wave loads
-constexpr int TPW = BM / (WAVES / 2);           // tokens (x rows) each wave computes
-constexpr int LOADS = RPW / RPI;                // load instructions per wave per stage
+// Small tiles: three 32 KiB stages.  Swept at 4096 -> 14336 bf16, one wave
+// per SIMD: 64 KiB (two stages) 66-68 us at M <= 128, 96 KiB 50-55, 128 KiB
+// the same as 96; at M = 192-256 two stages won (77-85 against 82-88 us),
+// where both lose to the unfused path anyway.
+#ifndef GLU_GEMM_SMALL_LDS
+#define GLU_GEMM_SMALL_LDS (96 * 1024)
+#endif
+#ifndef GLU_GEMM_SMALL_OCC
+#define GLU_GEMM_SMALL_OCC 1
+#endif
+using CfgLarge = GemmCfg<256, 128, GLU_GEMM_WAVES, 2, 128 * 1024, 1>;
+using CfgSmall = GemmCfg<128, 64, 4, 2, GLU_GEMM_SMALL_LDS, GLU_GEMM_SMALL_OCC>;
+
+constexpr int BK = kGemmBK;
+constexpr int ROW_BYTES = BK * 2;               // one row of a stage
+constexpr int CPR = BK / 8;                     // 16-byte chunks per row
+constexpr int RPI = 1024 / ROW_BYTES;           // rows per wave load instruction (1 KiB)
 constexpr int KSTEPS = BK / KD;                 // MFMA k steps per stage
-constexpr int FX = TPW / MF;                    // x (token) fragments per wave
-constexpr int FW = 64 / MF;                     // gate (and up) fragments per wave
-constexpr int NREAD = FX + 2 * FW;              // fragment reads per k step
-constexpr int NMFMA = FX * 2 * FW;              // MFMAs per k step
-static_assert(NST >= 2 && NST <= 4, "two to four stages");
 static_assert(KSTEPS % 2 == 0, "fragment double buffer alternates within a stage");
 
 // Chunk c of stage row r sits at position c ^ swz(r) of the row.  The 16
@@ -112,9 +127,26 @@ __device__ inline void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <typename E, int KIND>
-__global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
+template <typename E, int KIND, typename C>
+__global__ void __launch_bounds__(64 * C::WAVES, C::OCC) gemm_glu_kernel(const GemmArgs p)
 {
+    constexpr int BM = C::BM, BN = C::BN, WAVES = C::WAVES, WN = C::WN, WM = WAVES / WN;
+    constexpr int ROWS = BM + 2 * BN;               // x rows, then gate rows, then up rows
+    constexpr int STAGE_BYTES = ROWS * ROW_BYTES;
+    constexpr int NST = C::LDS_BYTES / STAGE_BYTES; // LDS stages, all in flight
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int RPW = ROWS / WAVES;               // stage rows each wave loads
+    constexpr int TPW = BM / WM;                    // tokens (x rows) each wave computes
+    constexpr int FPW = BN / WN;                    // features (of g and of u) each wave computes
+    constexpr int LOADS = RPW / RPI;                // load instructions per wave per stage
+    constexpr int FX = TPW / MF;                    // x (token) fragments per wave
+    constexpr int FW = FPW / MF;                    // gate (and up) fragments per wave
+    constexpr int NREAD = FX + 2 * FW;              // fragment reads per k step
+    constexpr int NMFMA = FX * 2 * FW;              // MFMAs per k step
+    static_assert(NST >= 2 && NST <= 4, "two to four stages");
+    static_assert(ROWS % WAVES == 0 && RPW % RPI == 0 && BM % RPW == 0 && BN % RPW == 0,
+                  "each wave loads whole instructions of one operand");
+    static_assert(TPW % MF == 0 && FPW % MF == 0 && NMFMA >= NREAD, "whole fragments per wave");
     __shared__ u32x4 lds_v[NST * STAGE_BYTES / 16];
     char *lds = reinterpret_cast<char *>(lds_v);
 
@@ -122,7 +154,7 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
     const TileCoord tc = grouped_coord(xcd_remap(blockIdx.x, nt), p.tiles_m, p.tiles_n, kGemmGroup);
     const int64_t m0 = int64_t(tc.r) * BM, n0 = int64_t(tc.c) * BN;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / WN, wn = w % WN;
 
     // Loads: wave w fills stage rows [RPW w, RPW w + RPW): x rows, then
     // gate rows, then up rows.  Instruction j covers rows
@@ -193,7 +225,7 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
     // chunk KD/8 * ks + lane / MF; row r, chunk c -> LDS byte
     // r*ROW_BYTES + 16*(c ^ swz(r)).
     const int kq = lane / MF;
-    const int ra = wm * TPW + (lane % MF), rg = BM + wn * 64 + (lane % MF), ru = BM + BN + wn * 64 + (lane % MF);
+    const int ra = wm * TPW + (lane % MF), rg = BM + wn * FPW + (lane % MF), ru = BM + BN + wn * FPW + (lane % MF);
     struct Frags {
         u32x4 a[FX], g[FW], u[FW];
     };
@@ -248,7 +280,8 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
                 __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NREAD, 0);
+            if constexpr (NMFMA > NREAD)
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NREAD, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -288,7 +321,8 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (LOADS + NREAD - 1) / NREAD, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NREAD, 0);
+        if constexpr (NMFMA > NREAD)
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NREAD, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
     for (; kt < KT; ++kt) {
@@ -320,7 +354,9 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     typedef E ex4 __attribute__((ext_vector_type(4)));
     constexpr int OPITCH = BN * 2 + 16;   // bytes per staged token row
+    constexpr int OCPR = BN / 8;          // 16-byte output chunks per token row
     static_assert(BM * OPITCH <= NST * STAGE_BYTES, "output tile fits the stage buffers");
+    static_assert((BM * OCPR) % THREADS == 0, "whole output chunks per thread");
     auto put = [&](E *dst, int64_t ld, auto value) {
         // this wave's values -> LDS
 #pragma unroll
@@ -334,15 +370,15 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
                     for (int t = 0; t < 4; ++t)
                         v4[t] = static_cast<E>(value(i, j, 4 * q + t));
                     const int row = wm * TPW + i * MF + (lane % MF);
-                    const int col = wn * 64 + j * MF + q * 8 + (lane >> 5) * 4;
+                    const int col = wn * FPW + j * MF + q * 8 + (lane >> 5) * 4;
                     *reinterpret_cast<u32x2 *>(lds + row * OPITCH + col * 2) = __builtin_bit_cast(u32x2, v4);
                 }
         __builtin_amdgcn_s_waitcnt(0);
         lds_barrier();
-        // LDS -> memory: chunk c covers token row c / 16, features 8 (c % 16) .. + 7
+        // LDS -> memory: chunk c covers token row c / OCPR, features 8 (c % OCPR) .. + 7
 #pragma unroll
-        for (int k = 0; k < BM * BN / 8 / THREADS; ++k) {
-            const int c = tid + THREADS * k, row = c >> 4, col = (c & 15) * 8;
+        for (int k = 0; k < BM * OCPR / THREADS; ++k) {
+            const int c = tid + THREADS * k, row = c / OCPR, col = (c % OCPR) * 8;
             const int64_t m = m0 + row, n = n0 + col;
             if (m >= p.M || n >= p.N)
                 continue;
@@ -373,25 +409,34 @@ __global__ void __launch_bounds__(THREADS, 1) gemm_glu_kernel(const GemmArgs p)
 
 typedef void (*GemmFn)(const GemmArgs);
 
-template <typename E> GemmFn pick_gemm(int kind)
+template <typename E, typename C> GemmFn pick_gemm(int kind)
 {
     switch (kind) {
-    case SILU: return &gemm_glu_kernel<E, SILU>;
-    case GELU_ERF: return &gemm_glu_kernel<E, GELU_ERF>;
-    case GELU_TANH: return &gemm_glu_kernel<E, GELU_TANH>;
-    default: return &gemm_glu_kernel<E, RELU>;
+    case SILU: return &gemm_glu_kernel<E, SILU, C>;
+    case GELU_ERF: return &gemm_glu_kernel<E, GELU_ERF, C>;
+    case GELU_TANH: return &gemm_glu_kernel<E, GELU_TANH, C>;
+    default: return &gemm_glu_kernel<E, RELU, C>;
     }
+}
+
+template <typename C> hipError_t launch_cfg(int dtype, int kind, const GemmArgs &args, hipStream_t stream)
+{
+    static_assert(C::BM == kGemmTiles[std::is_same<C, CfgSmall>::value ? kGemmSmall : kGemmLarge].bm &&
+                      C::BN == kGemmTiles[std::is_same<C, CfgSmall>::value ? kGemmSmall : kGemmLarge].bn,
+                  "the host plans tiles with the same shape");
+    GemmFn fn = dtype == F16 ? pick_gemm<_Float16, C>(kind) : pick_gemm<__bf16, C>(kind);
+    GemmArgs copy = args;
+    void *kargs[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(args.tiles_m * args.tiles_n), dim3(64 * C::WAVES),
+                           kargs, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_glu(int dtype, int kind, const GemmArgs &args, hipStream_t stream)
 {
-    GemmFn fn = dtype == F16 ? pick_gemm<_Float16>(kind) : pick_gemm<__bf16>(kind);
-    GemmArgs copy = args;
-    void *kargs[] = {&copy};
-    return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(args.tiles_m * args.tiles_n), dim3(THREADS), kargs, 0,
-                           stream);
+    return args.config == kGemmSmall ? launch_cfg<CfgSmall>(dtype, kind, args, stream)
+                                     : launch_cfg<CfgLarge>(dtype, kind, args, stream);
 }
 
 }  // namespace glu

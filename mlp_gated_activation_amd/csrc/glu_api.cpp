@@ -434,7 +434,9 @@ glu_status glu_gemm_fwd(glu_kind kind, glu_dtype dtype, int64_t M, int64_t N, in
         (ph & 1) || (pgu & 1))
         return GLU_ERR_ARG;
     const int64_t in_rows = K == 0 ? 0 : 1;   // inputs take no bytes when K == 0
-    const int64_t tm = (M + glu::kGemmBM - 1) / glu::kGemmBM, tn = (N + glu::kGemmBN - 1) / glu::kGemmBN;
+    const int cfg = glu::gemm_config(M);
+    const int64_t bm = glu::kGemmTiles[cfg].bm, bn = glu::kGemmTiles[cfg].bn;
+    const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
     if (tm * tn > int64_t(glu::kMaxGemmTiles) || ldx >= glu::kGemmMaxLd || ldwg >= glu::kGemmMaxLd ||
         ldwu >= glu::kGemmMaxLd)
         return GLU_ERR_SHAPE;
@@ -471,6 +473,7 @@ glu_status glu_gemm_fwd(glu_kind kind, glu_dtype dtype, int64_t M, int64_t N, in
     a.K = int32_t(K);
     a.tiles_m = uint32_t(tm);
     a.tiles_n = uint32_t(tn);
+    a.config = cfg;
     return glu::launch_gemm_glu(dtype, kind, a, stream) == hipSuccess ? GLU_OK : GLU_ERR_HIP;
 }
 

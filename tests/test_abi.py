@@ -361,8 +361,9 @@ def test_tile_kernel_isa():
 
 @pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="needs hipcc")
 def test_gemm_kernel_isa():
-    """The gate/up GEMM kernels: 8 instances (bf16/fp16 x 4 kinds), MFMA in
-    the k loop, no scratch, no packed fp32, LDS within the 160 KiB of a CU."""
+    """The gate/up GEMM kernels: 16 instances (bf16/fp16 x 4 kinds x the
+    large and small tile configurations), MFMA in the k loop, no scratch, no
+    packed fp32, LDS within the 160 KiB of a CU."""
     from mlp_gated_activation_amd import build as b
     src = [s for s in b.SOURCES if s.endswith("gemm_kernels.hip")][0]
     with tempfile.TemporaryDirectory() as tmp:
@@ -371,7 +372,7 @@ def test_gemm_kernel_isa():
         subprocess.run(cmd, cwd=tmp, check=True, capture_output=True)
         asm = open(os.path.join(tmp, "gemm_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")).read()
     names = re.findall(r"^(_Z\w*gemm_glu_kernel\w*):", asm, re.M)
-    assert len(names) == 8
+    assert len(names) == 16
     for name in names:
         pos = asm.find(name + ":")
         body = asm[pos:asm.find("s_endpgm", pos)]

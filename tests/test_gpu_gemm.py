@@ -50,11 +50,13 @@ def check_h(h, x, wg, wu, kind, what, min_one_ulp=0.99):
     return ref, g, u, one
 
 
+@pytest.mark.parametrize("M", [300, 150], ids=["large-tiles", "small-tiles"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("kind", KINDS)
-def test_ragged_tiles(glu, kind, dtype):
-    """M, N, K spanning several workgroup tiles and k stages, all ragged."""
-    M, N, K = 300, 200, 136
+def test_ragged_tiles(glu, kind, dtype, M):
+    """M, N, K spanning several workgroup tiles and k stages, all ragged, on
+    the large-tile (M > 256) and the small-tile (M <= 256) configuration."""
+    N, K = 200, 136
     x, w = inputs.gemm_glu(M, N, K, "bf16" if dtype == torch.bfloat16 else "fp16", w_std=0.1, seed=3)
     gx, gw = x.cuda(), w.cuda()
     h, gu = glu.glu_gemm_fwd(kind, gx, gw, gu=True)
@@ -162,15 +164,42 @@ def test_full_size_exact_sums(glu, kind, dtype):
     assert mx <= 1.0
 
 
+@pytest.mark.parametrize("M", [300, 200], ids=["large-tiles", "small-tiles"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("kind", KINDS)
-def test_exact_sums_every_kind(glu, kind, dtype):
-    """All eight (kind, dtype) pairs on exact-sum inputs over ragged tiles."""
-    M, N, K = 300, 200, 1032
+def test_exact_sums_every_kind(glu, kind, dtype, M):
+    """All eight (kind, dtype) pairs on exact-sum inputs over ragged tiles,
+    on both tile configurations."""
+    N, K = 200, 1032
     x, w = inputs.gemm_glu_exact(M, N, K, dtype, seed=4)
     h, gu = glu.glu_gemm_fwd(kind, x.cuda(), w.cuda(), gu=True)
     torch.cuda.synchronize()
     full_output_check(kind, dtype, h.cpu(), gu.cpu(), x, w, strict=True)
+
+
+@pytest.mark.parametrize("M", [16, 128, 256])
+def test_few_tokens_full_width(glu, M):
+    """The small-tile configuration at the benchmark's widths (hidden 4096,
+    I = 14336): exact-sum inputs within one output ulp everywhere, Gaussian
+    inputs within the contract bound, and both bit-identical to the
+    large-tile configuration (same k order), reached here through rows of a
+    larger call."""
+    N, K = 14336, 4096
+    x, w = inputs.gemm_glu_exact(M, N, K, "bf16", seed=6)
+    h, gu = glu.glu_gemm_fwd("silu", x.cuda(), w.cuda(), gu=True)
+    torch.cuda.synchronize()
+    full_output_check("silu", "bf16", h.cpu(), gu.cpu(), x, w, strict=True)
+    x, w = inputs.gemm_glu(M, N, K, "bf16", seed=6)
+    gx, gw = x.cuda(), w.cuda()
+    h, gu = glu.glu_gemm_fwd("gelu_tanh", gx, gw, gu=True)
+    torch.cuda.synchronize()
+    full_output_check("gelu_tanh", "bf16", h.cpu(), gu.cpu(), x, w, strict=False)
+    # the same rows inside a call of more than 256 tokens take the large tiles
+    big = gx.repeat(-(-300 // M), 1)
+    assert big.shape[0] > 256
+    hb = glu.glu_gemm_fwd("gelu_tanh", big, gw)
+    torch.cuda.synchronize()
+    assert torch.equal(hb[:M], h), "small and large tiles differ"
 
 
 @pytest.mark.parametrize("kind,dtype", FULL)
