@@ -162,6 +162,38 @@ def test_gated_mlp_fused_epilogue(fn, kind):
     assert _rel(w.grad, rw[0].grad) < tol
 
 
+@pytest.mark.parametrize("kind", KINDS)
+def test_gated_mlp_auto_epilogue(fn, kind):
+    """The default fused_epilogue="auto": the fused gate/up kernel for at most
+    128 tokens of bf16/fp16, the unfused path otherwise; both agree with the
+    float64 reference, in output and every gradient."""
+    torch.manual_seed(59)
+    hidden, inter = 256, 1000
+    mlp = fn.GatedMLP(hidden, inter, kind=kind, device="cuda", dtype=torch.bfloat16)
+    w = mlp.gate_up_proj.weight
+    for tokens, fused in ((16, True), (128, True), (129, False), (300, False)):
+        x = torch.randn(tokens, hidden, device="cuda", dtype=torch.bfloat16).requires_grad_()
+        assert mlp.uses_fused_epilogue(x) is fused, tokens
+        for q in mlp.parameters():
+            q.grad = None
+        out = mlp(x)
+        dout = torch.randn_like(out)
+        out.backward(dout)
+        rx, rw, rd, rout = _reference_mlp(x, [w], mlp.down_proj.weight, kind, True, inter)
+        rout.backward(dout.detach().cpu().double())
+        tol = 2e-2
+        assert _rel(out, rout) < tol, tokens
+        assert _rel(x.grad, rx.grad) < tol, tokens
+        assert _rel(mlp.down_proj.weight.grad, rd.grad) < tol, tokens
+        assert _rel(w.grad, rw[0].grad) < tol, tokens
+    # not for fp32, nor for a row stride the kernel cannot take
+    assert not fn.GatedMLP(hidden, inter, device="cuda").uses_fused_epilogue(torch.randn(16, hidden, device="cuda"))
+    xs = torch.randn(16, hidden + 4, device="cuda", dtype=torch.bfloat16)[:, :hidden]
+    assert not mlp.uses_fused_epilogue(xs)
+    assert not fn.GatedMLP(hidden, inter, fused_epilogue=False, device="cuda",
+                           dtype=torch.bfloat16).uses_fused_epilogue(x[:16])
+
+
 def test_gate_up_activation_inference_saves_nothing(fn):
     """Without gradients the forward writes no pre-activations."""
     x = torch.randn(64, 128, device="cuda", dtype=torch.bfloat16)

@@ -70,3 +70,19 @@ def test_nested_prefix():
           "mlp.down_proj.weight": torch.randn(8, 12, generator=g)}
     parent.load_state_dict(dict(sd))
     assert torch.equal(parent.mlp.gate_up_proj.weight[12:], sd["mlp.up_proj.weight"])
+
+
+def test_fused_epilogue_modes():
+    """fused_epilogue takes True, False or "auto" (the default); "auto" never
+    picks the fused GEMM for CPU tensors, and combines with
+    recompute_activation (which then wins)."""
+    m = F.GatedMLP(64, 96)
+    assert m.fused_epilogue == "auto"
+    assert not m.uses_fused_epilogue(torch.randn(4, 64, dtype=torch.bfloat16))
+    r = F.GatedMLP(64, 96, recompute_activation=True)
+    assert not r.uses_fused_epilogue(torch.randn(4, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        F.GatedMLP(64, 96, fused_epilogue="yes")
+    with pytest.raises(ValueError):
+        F.GatedMLP(64, 96, fused_gate_up=False, fused_epilogue=True)
+    F.GatedMLP(64, 96, fused_gate_up=False)   # "auto" needs no fused [gate | up]
