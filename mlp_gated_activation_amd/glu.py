@@ -143,12 +143,52 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+# Fast path of glu_fwd / glu_bwd for the common call: 2-D tensors with a
+# contiguous last dimension, one dtype, all on the current device, torch's
+# current stream.  It makes the same checks as the general path with fewer
+# Python operations (a call through the general path costs about 8 us of host
+# time, of which the library call and the kernel launch are about 3.7); any
+# call it does not cover, errors included, goes through the general path.
+_get_device = getattr(torch._C, "_cuda_getDevice", None)
+_fast = _raw_stream is not None and _get_device is not None
+
+
+def _rowmajor2(t, shape, dtype, dev):
+    return (t.dim() == 2 and t.dtype == dtype and t.get_device() == dev and t.shape == shape
+            and (t.stride(1) == 1 or shape[1] <= 1))
+
+
+def _ld2(t, rows, cols):
+    return t.stride(0) if rows > 1 else cols
+
+
 def glu_fwd(kind: str, layout: str, a: torch.Tensor, b: torch.Tensor | None = None,
             y: torch.Tensor | None = None, inplace: bool = False, stream=None) -> torch.Tensor:
     """y = act(a) * b.  layout "separate": a, b of shape (..., I).
     layout "gate_up": a is x of shape (..., 2I), b is None.
     inplace: the result overwrites b (separate) or x[..., I:] (gate_up) and
     that tensor (view) is returned; otherwise y (allocated if None) is."""
+    if stream is None and layout == "separate" and b is not None and _fast:
+        k, dt, dev, shape = KINDS.get(kind), DTYPES.get(a.dtype), a.get_device(), a.shape
+        if (k is not None and dt is not None and dev >= 0 and dev == _get_device()
+                and _rowmajor2(a, shape, a.dtype, dev) and _rowmajor2(b, shape, a.dtype, dev)):
+            rows, cols = shape
+            if inplace:
+                if y is None:
+                    st = _lib.glu_fwd(k, 0, dt, rows, cols, a.data_ptr(), _ld2(a, rows, cols), b.data_ptr(),
+                                      _ld2(b, rows, cols), None, 0, 1, _raw_stream(dev))
+                    if st != 0:
+                        raise GluError(st, "glu_fwd")
+                    return b
+            else:
+                if y is None:
+                    y = a.new_empty(shape)     # a's dtype and device, contiguous
+                if _rowmajor2(y, shape, a.dtype, dev):
+                    st = _lib.glu_fwd(k, 0, dt, rows, cols, a.data_ptr(), _ld2(a, rows, cols), b.data_ptr(),
+                                      _ld2(b, rows, cols), y.data_ptr(), _ld2(y, rows, cols), 0, _raw_stream(dev))
+                    if st != 0:
+                        raise GluError(st, "glu_fwd")
+                    return y
     k = _code(KINDS, kind, "kind")
     lay = _code(LAYOUTS, layout, "layout")
     dt = _code(DTYPES, a.dtype, "dtype")
@@ -203,6 +243,18 @@ def glu_bwd(kind: str, layout: str, a: torch.Tensor, b: torch.Tensor | None, dy:
     separate: returns (da, db); with inplace they are a and b themselves.
     gate_up: a is x (..., 2I), b is None; returns dx = [da | db] of x's shape
     (x itself when inplace; otherwise `da` is dx, allocated if None)."""
+    if stream is None and inplace and layout == "separate" and b is not None and da is None and db is None and _fast:
+        k, dt, dev, shape = KINDS.get(kind), DTYPES.get(a.dtype), a.get_device(), a.shape
+        if (k is not None and dt is not None and dev >= 0 and dev == _get_device()
+                and _rowmajor2(a, shape, a.dtype, dev) and _rowmajor2(b, shape, a.dtype, dev)
+                and _rowmajor2(dy, shape, a.dtype, dev)):
+            rows, cols = shape
+            st = _lib.glu_bwd(k, 0, dt, rows, cols, a.data_ptr(), _ld2(a, rows, cols), b.data_ptr(),
+                              _ld2(b, rows, cols), dy.data_ptr(), _ld2(dy, rows, cols), None, 0, None, 0, 1,
+                              _raw_stream(dev))
+            if st != 0:
+                raise GluError(st, "glu_bwd")
+            return a, b
     k = _code(KINDS, kind, "kind")
     lay = _code(LAYOUTS, layout, "layout")
     dt = _code(DTYPES, a.dtype, "dtype")
