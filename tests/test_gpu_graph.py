@@ -68,6 +68,16 @@ def test_graph_replay_strided_gemm_rmsnorm(glu):
     hr = torch.empty_like(xr)
     yr = torch.empty_like(xr)
     rstd = torch.empty(RR, dtype=torch.float32, device=dev)
+    # the few-token GEMM tiles (M <= 256) and the multi-row add + RMSNorm
+    # kernel (8192-wide rows, 37 rows over 10 workgroups)
+    Ms = 100
+    hs = torch.empty(Ms, N, dtype=t, device=dev)
+    RW, HW = 37, 8192
+    xw = torch.empty(RW, HW, dtype=t, device=dev)
+    rw = torch.empty_like(xw)
+    gw = torch.empty(HW, dtype=t, device=dev)
+    hw = torch.empty_like(xw)
+    yw = torch.empty_like(xw)
 
     def refill():
         a.copy_(torch.randn(R, C, device=dev, generator=g) * 2)
@@ -78,27 +88,33 @@ def test_graph_replay_strided_gemm_rmsnorm(glu):
         xr.copy_(torch.randn(RR, H, device=dev, generator=g))
         res.copy_(torch.randn(RR, H, device=dev, generator=g))
         gamma.copy_(1 + 0.1 * torch.randn(H, device=dev, generator=g))
+        xw.copy_(torch.randn(RW, HW, device=dev, generator=g))
+        rw.copy_(torch.randn(RW, HW, device=dev, generator=g))
+        gw.copy_(1 + 0.1 * torch.randn(HW, device=dev, generator=g))
 
-    def launch(out_y, out_da, out_db, out_h, out_gu, out_hr, out_yr, out_rstd):
+    def launch(out_y, out_da, out_db, out_h, out_gu, out_hr, out_yr, out_rstd, out_hs, out_hw, out_yw):
         glu.glu_fwd_strided("silu", a, b, out_y)
         glu.glu_bwd_strided("gelu_erf", a, b, dy, out_da, out_db)
         glu.glu_gemm_fwd("silu", x, w, h=out_h, gu=out_gu)
         glu.glu_add_rmsnorm_fwd(xr, res, gamma, 1e-6, h=out_hr, y=out_yr, rstd=out_rstd)
+        glu.glu_gemm_fwd("gelu_tanh", x[:Ms], w, h=out_hs)
+        glu.glu_add_rmsnorm_fwd(xw, rw, gw, 1e-6, h=out_hw, y=out_yw)
 
+    outs = (y, da, db, h, gu, hr, yr, rstd, hs, hw, yw)
     refill()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        launch(y, da, db, h, gu, hr, yr, rstd)
-    eager = [torch.empty_like(v) for v in (y, da, db, h, gu, hr, yr, rstd)]
+        launch(*outs)
+    eager = [torch.empty_like(v) for v in outs]
     for rep in range(4):
         refill()
         graph.replay()
         torch.cuda.synchronize()
         launch(*eager)
         torch.cuda.synchronize()
-        for got, want, nm in zip((y, da, db, h, gu, hr, yr, rstd), eager,
-                                 ("y", "da", "db", "h", "gu", "h (norm)", "y (norm)", "rstd")):
+        for got, want, nm in zip(outs, eager, ("y", "da", "db", "h", "gu", "h (norm)", "y (norm)", "rstd",
+                                               "h (few tokens)", "h (8192-wide norm)", "y (8192-wide norm)")):
             assert same_bits(got, want), f"replay {rep}: {nm} differs from the eager launch"
 
     # the eager results of the last round against the oracle
@@ -118,3 +134,10 @@ def test_graph_replay_strided_gemm_rmsnorm(glu):
     ref = oracle.add_rmsnorm(f64(xr), f64(res), f64(gamma), 1e-6)
     rep = compare(f64(yr), ref[1], FMT[yr.dtype])
     assert rep.ok, f"add_rmsnorm y: {rep}"
+    ref = oracle.add_rmsnorm(f64(xw), f64(rw), f64(gw), 1e-6)
+    for got, want, nm in ((hw, ref[0], "h"), (yw, ref[1], "y")):
+        rep = compare(f64(got), want, FMT[got.dtype])
+        assert rep.ok, f"8192-wide add_rmsnorm {nm}: {rep}"
+    rhs, _, _ = oracle.gemm_glu("gelu_tanh", f64(x[:Ms]), f64(w[:N]), f64(w[N:]), want_gu=True)
+    err = np.abs(f64(hs) - rhs)
+    assert float(np.max(err / np.maximum(np.abs(rhs), 1e-3))) < 2 ** -6, "few-token GEMM h far from the oracle"
