@@ -44,6 +44,7 @@ KERNEL_SOURCES = ["mlp_gated_activation_amd/csrc/glu_kernels.hip",
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_glu_swiglu_bf16_4096x14336.md")
 TILE_PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_glu_tile_swiglu_bf16_4096x14336_dyT.md")
 GEMM_SOURCES = ["mlp_gated_activation_amd/csrc/gemm_kernels.hip",
+                "mlp_gated_activation_amd/csrc/gemm_internal.h",
                 "mlp_gated_activation_amd/csrc/glu_act.h",
                 "mlp_gated_activation_amd/csrc/glu_internal.h",
                 "mlp_gated_activation_amd/csrc/glu_taylor.h",

@@ -38,6 +38,7 @@
 
 #include "glu_act.h"
 #include "glu_internal.h"
+#include "gemm_internal.h"
 
 namespace glu {
 namespace {

@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include "glu_internal.h"
+#include "gemm_internal.h"
 #include "rmsnorm_internal.h"
 
 namespace {

@@ -11,6 +11,7 @@
 // prints "ok <launches>" or "FAIL <reason>".
 #include "glu.h"
 #include "glu_internal.h"
+#include "gemm_internal.h"
 #include "rmsnorm_internal.h"
 
 #include <cstdio>

@@ -18,6 +18,7 @@
 // prints "<status> <path> <launches>" or "FAIL <reason>".
 #include "glu.h"
 #include "glu_internal.h"
+#include "gemm_internal.h"
 #include "rmsnorm_internal.h"
 
 #include <cstdio>

@@ -274,6 +274,7 @@ def test_gemm_tile_order_is_a_bijection():
     do not divide by the 8 XCDs or the group height."""
     src = r"""
 #include "glu_internal.h"
+#include "gemm_internal.h"
 #include <cstdio>
 #include <vector>
 int main() {
