@@ -36,11 +36,11 @@ extern "C" {
 #endif
 
 /* The forward's mix: read a and b, write y (2:1).  Launch shape of the
- * 16-bit SiLU/ReLU forward. */
+ * 16-bit forward. */
 GLU_REF_API int glu_ref_fwd_mix(const void *a, const void *b, void *y, uint64_t bytes, hipStream_t stream);
 
 /* The backward's mix: read a, b and dy, write da and db (3:2).  Launch shape
- * of the 16-bit SiLU/ReLU backward. */
+ * of the 16-bit backward. */
 GLU_REF_API int glu_ref_bwd_mix(const void *a, const void *b, const void *dy, void *da, void *db,
                                 uint64_t bytes, hipStream_t stream);
 

@@ -49,8 +49,8 @@ namespace glu {
 
 // LDS reserved per workgroup (never accessed) to cap the workgroups resident
 // on a CU, 160 KiB of LDS each: 25 forward (64 threads), 10 backward (128
-// threads).  Applied to SiLU and ReLU on 16-bit data in launches of at least
-// kCapMinUnits units; the launcher in glu_kernels.hip gives the measurements.
+// threads).  Applied to 16-bit data in launches of at least kCapMinUnits
+// units; the launcher in glu_kernels.hip gives the measurements.
 constexpr unsigned kCapLdsFwd = 6400, kCapLdsBwd = 16384;
 #ifndef GLU_CAP_MIN_UNITS
 #define GLU_CAP_MIN_UNITS (1u << 22)

@@ -512,20 +512,22 @@ hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args
     dim3 block(bs);
     Args copy = args;
     void *kargs[] = {&copy};
-    // The kernels use no LDS; for SiLU and ReLU on 16-bit data, reserving
-    // some caps the workgroups resident on a CU (160 KiB of LDS each): 25
-    // forward (64 threads), 10 backward (128 threads).  Fewer streams in
-    // flight per CU moved more bytes on MI355X: bf16 SwiGLU 4096 x 14336 fwd
-    // 6521 -> 6643 GB/s, bwd 6380 -> 6470; fp16 [gate | up] 8191 x 18944
-    // ReGLU fwd 6702 -> 6783, bwd 6466 -> 6602.  At 24 forward workgroups per
-    // CU the forward falls back.  The GELU backwards, with more arithmetic per
-    // element, lost 4 % capped (fp16 [gate | up] 8191 x 18944), and fp32 data
-    // (fp64 arithmetic) lost up to 8 %: those keep every workgroup they can.
-    // Small launches, too: below 2^22 units (4096 x 8192 bf16) the cap leaves
-    // a second, partial round of workgroups, and uncapped they ran 2-3.5 %
-    // faster at 4096 x 512 .. 3072 (even at 4096 x 4096 .. 6144), while the
-    // cap gained 1 % from 4096 x 8192 up.
-    const bool cap = dtype != F32 && (kind == SILU || kind == RELU) && args.units >= kCapMinUnits;
+    // The kernels use no LDS; on 16-bit data, reserving some caps the
+    // workgroups resident on a CU (160 KiB of LDS each): 25 forward (64
+    // threads), 10 backward (128 threads).  Fewer streams in flight per CU
+    // moved more bytes on MI355X: bf16 SwiGLU 4096 x 14336 fwd 6521 -> 6643
+    // GB/s, bwd 6380 -> 6470; fp16 [gate | up] 8191 x 18944 ReGLU fwd 6702 ->
+    // 6783, bwd 6466 -> 6602; and, with inputs restored between timed
+    // batches, the GELU kinds 1-2.5 % in both directions (bf16 4096 x 14336
+    // GELU-erf fwd 6399 -> 6515, bwd 6341 -> 6408; fp16 [gate | up] 8191 x
+    // 18944 GELU-erf fwd 6639 -> 6808, bwd 6434 -> 6552; GELU-tanh alike).
+    // At 24 forward workgroups per CU the forward falls back.  fp32 data
+    // (fp64 arithmetic) lost up to 8 % capped and keeps every workgroup it
+    // can.  Small launches, too: below 2^22 units (4096 x 8192 bf16) the cap
+    // leaves a second, partial round of workgroups, and uncapped they ran
+    // 2-3.5 % faster at 4096 x 512 .. 3072 (even at 4096 x 4096 .. 6144),
+    // while the cap gained 1 % from 4096 x 8192 up.
+    const bool cap = dtype != F32 && args.units >= kCapMinUnits;
     const unsigned lds = !cap ? 0u : backward ? kCapLdsBwd : kCapLdsFwd;
     return hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block, kargs, lds, stream);
 }
