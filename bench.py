@@ -448,12 +448,13 @@ def main():
 
 
 def bench_providers(args, torch, glu, inputs, dev):
-    """The SwiGLU op over the pages' benchmark sweep ("LigerSiLUMulFunction",
+    """The SwiGLU op over the pages' benchmark sweep ("Kernel Profile: SwiGLU",
     Benchmarking: hidden size 1024 .. 16384, 4096 rows, bf16; providers this
     library, torch eager and torch.compile), forward and full (forward then
-    backward).  Every provider is launched call by call from Python, as a
-    training loop would; for this library a HIP graph of the same calls is
-    timed as well.  Buffer sets rotate over at least 1 GiB, so every call
+    backward), plus H = 1792, one rank's share of the 14336-wide activation
+    under 8-way tensor parallelism.  Every provider is launched call by call
+    from Python, as a training loop would; for this library a HIP graph of
+    the same calls is timed as well.  Buffer sets rotate over at least 1 GiB, so every call
     streams from HBM.  Context only: the headline is the default op."""
     import torch.nn.functional as F
     stream = torch.cuda.current_stream(dev)
@@ -467,7 +468,9 @@ def bench_providers(args, torch, glu, inputs, dev):
 
     rows_out = []
     compile_error = None
-    for h in (1024, 2048, 4096, 8192, 16384):
+    sweep = [(h, f"swiglu_bf16_4096x{h}") for h in (1024, 2048, 4096, 8192, 16384)]
+    sweep.insert(1, (1792, "swiglu_bf16_tp8_4096x1792"))     # one TP = 8 rank's share of 14336
+    for h, wname in sweep:
         # a fresh compilation per size: the guard cache of one compiled
         # function would otherwise fill up and fall back to eager silently
         try:
@@ -475,7 +478,7 @@ def bench_providers(args, torch, glu, inputs, dev):
             cfwd = torch.compile(lambda a, b: F.silu(a) * b, dynamic=False)
         except Exception as e:   # context only
             cfwd, compile_error = None, f"{type(e).__name__}: {e}"[:300]
-        w = inputs.WORKLOADS[f"swiglu_bf16_4096x{h}"]
+        w = inputs.WORKLOADS[wname]
         a_h, b_h, dy_h = w.make(seed=0)
         n = a_h.numel()
         nsets = max(2, -(-(1 << 30) // (4 * n * 2)))
@@ -531,7 +534,7 @@ def bench_providers(args, torch, glu, inputs, dev):
             r = max(1, reps // nsets)
             return timed(lambda i: g.replay(), r, batch=1) / nsets
 
-        row = {"H": h, "bytes_fwd": fwd_bytes, "bytes_full": step_bytes}
+        row = {"H": h, "workload": wname, "bytes_fwd": fwd_bytes, "bytes_full": step_bytes}
         legs = [("ours", ours_fwd, ours_step), ("torch", eager_fwd, eager_step)]
         if cfwd is not None:
             legs.append(("torch_compile", comp_fwd, comp_step))
@@ -569,7 +572,8 @@ def bench_providers(args, torch, glu, inputs, dev):
         "dtype": "bf16",
         "data": "synthetic (seeded a~N(0,4), b,dy~N(0,1) rounded to bf16; >= 1 GiB of rotating buffer sets; "
                 "a, b restored from a pristine device copy between timed batches, untimed)",
-        "config": {"workload": "SwiGLU bf16 separate a,b,dy (4096, H), H = 1024 .. 16384; value at H = 16384",
+        "config": {"workload": "SwiGLU bf16 separate a,b,dy (4096, H), H = 1024 .. 16384 and 1792 (one "
+                               "TP = 8 rank's share of 14336); value at H = 16384",
                    "providers": ["ours", "torch", "torch_compile", "ours_hip_graph"]},
         "sweep": rows_out,
         # context only: the headline op carries the oracle's CPU timing

@@ -166,6 +166,8 @@ WORKLOADS = {
                  notes="fused [gate|up] x of shape (4096, 28672)"),
         *[Workload(f"swiglu_bf16_4096x{h}", ("silu",), "bf16", "separate", 4096, h, 2.0,
                    notes="hidden-size sweep") for h in (1024, 2048, 4096, 8192, 16384)],
+        Workload("swiglu_bf16_tp8_4096x1792", ("silu",), "bf16", "separate", 4096, 1792, 2.0,
+                 notes="one tensor-parallel rank's share of I = 14336 at TP = 8"),
         Workload("geglu_reglu_fp16_gateup_8191x18944", ("gelu_erf", "gelu_tanh", "relu"), "fp16",
                  "gate_up", 8191, 18944, 1.0, stress=True,
                  notes="odd row count, Qwen2-7B-like width, 1% large gate values"),

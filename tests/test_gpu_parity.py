@@ -118,9 +118,10 @@ def test_bf16_gate_up_4096x14336(glu):
     check(gx, rdx, "gate_up bwd in-place dx")
 
 
-@pytest.mark.parametrize("h", [1024, 2048, 4096, 8192, 16384])
-def test_bf16_hidden_sweep(glu, h):
-    w = inputs.WORKLOADS[f"swiglu_bf16_4096x{h}"]
+@pytest.mark.parametrize("name", [f"swiglu_bf16_4096x{h}" for h in (1024, 2048, 4096, 8192, 16384)]
+                         + ["swiglu_bf16_tp8_4096x1792"])
+def test_bf16_hidden_sweep(glu, name):
+    w = inputs.WORKLOADS[name]
     a, b, dy = w.make()
     _separate_fwd_bwd(glu, "silu", a, b, dy, w.name, bwd_out_of_place=False)
 
