@@ -24,6 +24,17 @@ namespace glu {
 #ifndef GLU_BLOCK_BWD
 #define GLU_BLOCK_BWD GLU_BLOCK
 #endif
+// Backward launches of fewer than kCapMinUnits units (below 4096 x 8192
+// bf16) finish in one or two rounds of workgroups, and there fewer, larger
+// blocks start the streams sooner: bf16 SwiGLU backward, 4096 rows, 512
+// against 128 threads (same process): 9.0 / 9.7 us at 1024 columns, 14.6 /
+// 15.5 at 1792, 16.2 / 17.0 at 2048, 29.8 / 30.6 at 4096, 43.0 / 43.3 at 6144.
+// From 4096 x 8192 up the capped 128-thread blocks are as fast or faster
+// (4096 x 11008: 73.3 / 72.4 us; 4096 x 14336: 94.1 / 93.4).  The forward
+// keeps 64 threads at every size (1024 columns: even with 256..1024).
+#ifndef GLU_BLOCK_BWD_SMALL
+#define GLU_BLOCK_BWD_SMALL 512
+#endif
 #ifndef GLU_UNROLL
 #define GLU_UNROLL 1
 #endif

@@ -163,15 +163,12 @@ __device__ inline const void *at(const void *base, int64_t off, int size)
 }
 __device__ inline void *at(void *base, int64_t off, int size) { return static_cast<char *>(base) + off * size; }
 
-template <bool BWD> constexpr int block_size() { return BWD ? GLU_BLOCK_BWD : GLU_BLOCK_FWD; }
-
-template <typename T, int KIND, bool BWD, bool VEC, bool FLAT>
-__global__ void __launch_bounds__(block_size<BWD>()) glu_kernel(const Args p)
+template <typename T, int KIND, bool BWD, bool VEC, bool FLAT, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) glu_kernel(const Args p)
 {
     using M = typename T::M;
     constexpr int VE = VEC ? T::VE : 1;
     constexpr int U = GLU_UNROLL;
-    constexpr int BLOCK = block_size<BWD>();
 
 #if GLU_XCD_REMAP
     // Blocks are dispatched round-robin over the 8 XCDs; give XCD x the
@@ -459,21 +456,31 @@ template <typename T, bool BWD> TileFn pick_tile(int kind)
 // ---------------------------------------------------------------------------
 typedef void (*KernelFn)(const Args);
 
-template <typename T, int KIND, bool BWD>
+template <typename T, int KIND, bool BWD, int BLOCK>
 constexpr KernelFn pick(bool vec, bool flat)
 {
-    return vec ? (flat ? &glu_kernel<T, KIND, BWD, true, true> : &glu_kernel<T, KIND, BWD, true, false>)
-               : (flat ? &glu_kernel<T, KIND, BWD, false, true> : &glu_kernel<T, KIND, BWD, false, false>);
+    return vec ? (flat ? &glu_kernel<T, KIND, BWD, true, true, BLOCK> : &glu_kernel<T, KIND, BWD, true, false, BLOCK>)
+               : (flat ? &glu_kernel<T, KIND, BWD, false, true, BLOCK> : &glu_kernel<T, KIND, BWD, false, false, BLOCK>);
+}
+
+// The forward has one block size; the backward a large-launch and a
+// small-launch one.
+template <typename T, int KIND>
+KernelFn pick_dir(bool bwd, bool small, bool vec, bool flat)
+{
+    if (!bwd)
+        return pick<T, KIND, false, GLU_BLOCK_FWD>(vec, flat);
+    return small ? pick<T, KIND, true, GLU_BLOCK_BWD_SMALL>(vec, flat) : pick<T, KIND, true, GLU_BLOCK_BWD>(vec, flat);
 }
 
 template <typename T>
-KernelFn pick_kind(int kind, bool bwd, bool vec, bool flat)
+KernelFn pick_kind(int kind, bool bwd, bool small, bool vec, bool flat)
 {
     switch (kind) {
-    case SILU: return bwd ? pick<T, SILU, true>(vec, flat) : pick<T, SILU, false>(vec, flat);
-    case GELU_ERF: return bwd ? pick<T, GELU_ERF, true>(vec, flat) : pick<T, GELU_ERF, false>(vec, flat);
-    case GELU_TANH: return bwd ? pick<T, GELU_TANH, true>(vec, flat) : pick<T, GELU_TANH, false>(vec, flat);
-    default: return bwd ? pick<T, RELU, true>(vec, flat) : pick<T, RELU, false>(vec, flat);
+    case SILU: return pick_dir<T, SILU>(bwd, small, vec, flat);
+    case GELU_ERF: return pick_dir<T, GELU_ERF>(bwd, small, vec, flat);
+    case GELU_TANH: return pick_dir<T, GELU_TANH>(bwd, small, vec, flat);
+    default: return pick_dir<T, RELU>(bwd, small, vec, flat);
     }
 }
 
@@ -503,10 +510,11 @@ hipError_t launch(int dtype, int kind, bool backward, bool vec, const Args &args
 {
     // a launch whose units all lie in one row needs no row division
     const bool flat = args.units == args.units_per_row;
-    KernelFn fn = dtype == F32 ? pick_kind<SF32>(kind, backward, vec, flat)
-                : dtype == F16 ? pick_kind<SF16>(kind, backward, vec, flat)
-                               : pick_kind<SBf16>(kind, backward, vec, flat);
-    const uint32_t bs = backward ? GLU_BLOCK_BWD : GLU_BLOCK_FWD;
+    const bool small = args.units < kCapMinUnits;
+    KernelFn fn = dtype == F32 ? pick_kind<SF32>(kind, backward, small, vec, flat)
+                : dtype == F16 ? pick_kind<SF16>(kind, backward, small, vec, flat)
+                               : pick_kind<SBf16>(kind, backward, small, vec, flat);
+    const uint32_t bs = !backward ? GLU_BLOCK_FWD : small ? GLU_BLOCK_BWD_SMALL : GLU_BLOCK_BWD;
     const uint32_t per_block = bs * GLU_UNROLL;
     dim3 grid((args.units + per_block - 1) / per_block);
     dim3 block(bs);

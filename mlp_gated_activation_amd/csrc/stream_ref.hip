@@ -185,15 +185,22 @@ GLU_REF_API int glu_ref_bwd_mix(const void *a, const void *b, const void *dy, vo
 {
     if (bad(a) || bad(b) || bad(dy) || bad(da) || bad(db) || (bytes & 15u) != 0)
         return -1;
-    constexpr int B = GLU_BLOCK_BWD;
     const uint64_t n = bytes / 16;
     const unsigned lds = cap_lds(n, glu::kCapLdsBwd);
+    // the streaming launcher's block size for the same unit count
+    const bool small = n < glu::kCapMinUnits;
     for (uint64_t v0 = 0; v0 < n; v0 += kMaxVecs) {
         const uint32_t m = uint32_t(n - v0 < kMaxVecs ? n - v0 : kMaxVecs);
-        hipLaunchKernelGGL(bwd_mix_kernel<B>, dim3((m + B - 1) / B), dim3(B), lds, stream,
-                           static_cast<const u32x4 *>(a) + v0, static_cast<const u32x4 *>(b) + v0,
-                           static_cast<const u32x4 *>(dy) + v0, static_cast<u32x4 *>(da) + v0,
-                           static_cast<u32x4 *>(db) + v0, m);
+        const u32x4 *pa = static_cast<const u32x4 *>(a) + v0, *pb = static_cast<const u32x4 *>(b) + v0,
+                    *pd = static_cast<const u32x4 *>(dy) + v0;
+        u32x4 *pda = static_cast<u32x4 *>(da) + v0, *pdb = static_cast<u32x4 *>(db) + v0;
+        if (small) {
+            constexpr int B = GLU_BLOCK_BWD_SMALL;
+            hipLaunchKernelGGL(bwd_mix_kernel<B>, dim3((m + B - 1) / B), dim3(B), lds, stream, pa, pb, pd, pda, pdb, m);
+        } else {
+            constexpr int B = GLU_BLOCK_BWD;
+            hipLaunchKernelGGL(bwd_mix_kernel<B>, dim3((m + B - 1) / B), dim3(B), lds, stream, pa, pb, pd, pda, pdb, m);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return int(e);

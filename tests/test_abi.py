@@ -314,7 +314,9 @@ def test_kernel_isa():
         asm = open(os.path.join(tmp, "glu_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")).read()
     unroll = int(re.search(r"#define GLU_UNROLL (\d+)", open(os.path.join(CSRC, "glu_internal.h")).read()).group(1))
     starts = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\w*glu_kernel\w*):", asm, re.M)]
-    assert len(starts) == 96
+    # 3 dtypes x 4 kinds x vector/element x flat/strided, forward at one
+    # block size and backward at two
+    assert len(starts) == 144
     assert set(re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)) == {"0"}, "a kernel uses scratch"
     # every kernel of the library: no MFMA, no packed fp32
     for name in re.findall(r"^(_Z\w+):", asm, re.M):
