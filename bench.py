@@ -220,6 +220,9 @@ def main():
                          "SwiGLU MLP training step (4096 tokens, 4096 -> 14336, bf16), GatedMLP against the "
                          "same network in torch, time and peak memory")
     ap.add_argument("--hidden", type=int, default=4096, help="add_rmsnorm only: row width")
+    ap.add_argument("--gemm-shapes", action="store_true",
+                    help="gemm_glu only: also time the fused and unfused paths at 1 .. 256 tokens over other "
+                         "MLP shapes (hidden x intermediate), with the choice GatedMLP's default makes")
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--sets", type=int, default=6, help="rotating buffer sets (470 MB each)")
@@ -894,6 +897,33 @@ def bench_strided(args, torch, glu, inputs, dev):
 PEAK_BF16_TFLOPS = 2500.0
 
 
+def gemm_shape_sweep(torch, glu, inputs, dev, timed):
+    """Fused against unfused gate/up projection at few tokens over several MLP
+    shapes, bf16 SwiGLU, with the path GatedMLP's default picks.  Weight
+    copies rotate over at least 1 GiB, so every call streams them from HBM."""
+    from mlp_gated_activation_amd.functional import fused_epilogue_wins
+    out = []
+    for K, N in ((4096, 11008), (5120, 13824), (8192, 28672), (3584, 18944), (2048, 8192)):
+        nw = max(2, -(-(1 << 30) // (2 * N * K * 2)))
+        x_h, w_h = inputs.gemm_glu(256, N, K, "bf16", seed=0)
+        ws = [w_h.to(dev) for _ in range(nw)]
+        x = x_h.to(dev)
+        for M in (1, 16, 64, 128, 256):
+            xs = x[:M]
+            hs = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            gus = torch.empty(M, 2 * N, dtype=torch.bfloat16, device=dev)
+            t_f = timed(lambda i: glu.glu_gemm_fwd("silu", xs, ws[i % nw], h=hs), 60)
+            t_u = timed(lambda i: (torch.matmul(xs, ws[i % nw].t(), out=gus),
+                                   glu.glu_fwd("silu", "gate_up", gus, y=hs)), 60)
+            out.append({"hidden": K, "intermediate": N, "M": M, "fused_us": round(1e3 * t_f, 1),
+                        "unfused_us": round(1e3 * t_u, 1), "speedup_vs_unfused": round(t_u / t_f, 3),
+                        "auto_picks_fused": fused_epilogue_wins(M, N, dev)})
+        del ws
+        torch.cuda.empty_cache()
+        print(f"gemm shapes: {K} x {N} done", file=sys.stderr, flush=True)
+    return out
+
+
 def bench_gemm(args, torch, glu, inputs, dev):
     """Gate/up projection with the activation fused into the GEMM epilogue
     ("Fused Kernels", section 4), bf16 SwiGLU: x (4096, 4096), fused
@@ -951,6 +981,7 @@ def bench_gemm(args, torch, glu, inputs, dev):
                         "weights_GBps_fused": round(2 * N * K * 2 / (t_f * 1e-3) / 1e9, 1)})
     del sets, gu, ws
     torch.cuda.empty_cache()
+    shape_sweep = gemm_shape_sweep(torch, glu, inputs, dev, timed) if args.gemm_shapes else None
     tf = lambda ms: round(flops / (ms * 1e-3) / 1e12, 1)
     value = tf(t_fused)
     result = {
@@ -974,6 +1005,7 @@ def bench_gemm(args, torch, glu, inputs, dev):
         },
         "speedup_vs_unfused": round(t_unfused / t_fused, 3),
         "m_sweep": m_sweep,
+        "shape_sweep": shape_sweep,
         "roofline": {"bound": "mfma", "kernel": "gemm_glu_kernel<bf16, silu>", "achieved": value,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
                      "traffic": committed_traffic(GEMM_PMC_SUMMARY, "traffic_bytes", GEMM_SOURCES)},

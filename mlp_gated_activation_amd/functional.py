@@ -33,6 +33,32 @@ import torch.nn as nn
 from . import glu as _glu
 
 _KINDS = ("silu", "gelu_erf", "gelu_tanh", "relu")
+
+# The fused gate/up kernel's few-token tile configuration (csrc/gemm_internal.h:
+# kGemmTiles[kGemmSmall] and kGemmSmallMaxM): 128 tokens x 64 features per
+# workgroup, taken for at most 256 tokens.
+_SMALL_TILE_TOKENS, _SMALL_TILE_FEATURES, _SMALL_MAX_TOKENS = 128, 64, 256
+_cu_count = {}
+
+
+def fused_epilogue_wins(tokens: int, intermediate: int, device) -> bool:
+    """Whether the fused gate/up kernel measured faster than the library GEMM
+    followed by the activation kernel, for this many tokens and this
+    intermediate width.  At few tokens both stream the weights once; the
+    fused kernel wins when its few-token tiles fill at most one round of
+    workgroups, one per compute unit, and loses when a second, partial
+    round follows (bf16, fused / unfused us at 1 .. 256 tokens, hidden x I:
+    4096 x 14336 1.02-1.23x up to 128 tokens, 224 workgroups, 0.80x at 256
+    with 448; 2048 x 8192 1.04-1.29x up to 256, at most 256 workgroups;
+    3584 x 18944 0.72-0.85x, 296 workgroups; 8192 x 28672 0.62-0.99x, 448)."""
+    if tokens <= 0 or tokens > _SMALL_MAX_TOKENS:
+        return False
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    if idx not in _cu_count:
+        _cu_count[idx] = torch.cuda.get_device_properties(idx).multi_processor_count
+    tiles = -(-tokens // _SMALL_TILE_TOKENS) * -(-intermediate // _SMALL_TILE_FEATURES)
+    return tiles <= _cu_count[idx]
 # Hugging Face activation names (a config's hidden_act) -> kinds: "gelu" is
 # the exact erf form; "gelu_new" and "gelu_pytorch_tanh" are the tanh form.
 HF_ACTIVATIONS = {"silu": "silu", "swish": "silu", "gelu": "gelu_erf", "gelu_new": "gelu_tanh",
@@ -263,11 +289,9 @@ class GatedMLP(nn.Module):
     projection and the activation in one kernel (gate_up_activation).
     fused_epilogue="auto" (the default) does so only where that kernel
     measured faster than the library GEMM followed by the separate activation
-    kernel: at most FUSED_EPILOGUE_MAX_TOKENS tokens (bf16, 4096 -> 14336:
-    1.03-1.10x at 16-128 tokens; 0.83x at 256 and 0.91x at 4096), with bf16
-    or fp16 operands that meet its alignment (see uses_fused_epilogue)."""
-
-    FUSED_EPILOGUE_MAX_TOKENS = 128
+    kernel (fused_epilogue_wins: few tokens, and few enough workgroups for
+    one round; at 4096 tokens the unfused path is 1.1x faster), with bf16 or
+    fp16 operands that meet its alignment (see uses_fused_epilogue)."""
 
     def __init__(self, hidden_size: int, intermediate_size: int, kind: str = "silu",
                  fused_gate_up: bool = True, inplace_backward: bool = True, fused_epilogue="auto",
@@ -333,7 +357,7 @@ class GatedMLP(nn.Module):
         if not (x.is_cuda and x.dtype in (torch.bfloat16, torch.float16) and w.dtype == x.dtype
                 and w.device == x.device and H % 8 == 0 and H > 0):
             return False
-        if x.numel() // H > self.FUSED_EPILOGUE_MAX_TOKENS:
+        if not fused_epilogue_wins(x.numel() // H, w.shape[0] // 2, x.device):
             return False
         # the kernel's operand rules: 16-byte aligned rows, row strides a multiple of 8
         x2 = x.reshape(-1, H)

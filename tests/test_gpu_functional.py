@@ -165,13 +165,14 @@ def test_gated_mlp_fused_epilogue(fn, kind):
 @pytest.mark.parametrize("kind", KINDS)
 def test_gated_mlp_auto_epilogue(fn, kind):
     """The default fused_epilogue="auto": the fused gate/up kernel for at most
-    128 tokens of bf16/fp16, the unfused path otherwise; both agree with the
-    float64 reference, in output and every gradient."""
+    256 tokens of bf16/fp16 whose few-token tiles fill at most one round of
+    workgroups, the unfused path otherwise; both agree with the float64
+    reference, in output and every gradient."""
     torch.manual_seed(59)
     hidden, inter = 256, 1000
     mlp = fn.GatedMLP(hidden, inter, kind=kind, device="cuda", dtype=torch.bfloat16)
     w = mlp.gate_up_proj.weight
-    for tokens, fused in ((16, True), (128, True), (129, False), (300, False)):
+    for tokens, fused in ((16, True), (129, True), (256, True), (257, False), (300, False)):
         x = torch.randn(tokens, hidden, device="cuda", dtype=torch.bfloat16).requires_grad_()
         assert mlp.uses_fused_epilogue(x) is fused, tokens
         for q in mlp.parameters():
@@ -186,6 +187,11 @@ def test_gated_mlp_auto_epilogue(fn, kind):
         assert _rel(x.grad, rx.grad) < tol, tokens
         assert _rel(mlp.down_proj.weight.grad, rd.grad) < tol, tokens
         assert _rel(w.grad, rw[0].grad) < tol, tokens
+    # not where the few-token tiles need more than one workgroup per compute unit
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    wide = fn.GatedMLP(hidden, 64 * ncu + 1, device="cuda", dtype=torch.bfloat16)
+    assert not wide.uses_fused_epilogue(x[:16])
+    assert fn.GatedMLP(hidden, 64 * ncu, device="cuda", dtype=torch.bfloat16).uses_fused_epilogue(x[:16])
     # not for fp32, nor for a row stride the kernel cannot take
     assert not fn.GatedMLP(hidden, inter, device="cuda").uses_fused_epilogue(torch.randn(16, hidden, device="cuda"))
     xs = torch.randn(16, hidden + 4, device="cuda", dtype=torch.bfloat16)[:, :hidden]

@@ -86,3 +86,28 @@ def test_fused_epilogue_modes():
     with pytest.raises(ValueError):
         F.GatedMLP(64, 96, fused_gate_up=False, fused_epilogue=True)
     F.GatedMLP(64, 96, fused_gate_up=False)   # "auto" needs no fused [gate | up]
+
+
+def test_fused_epilogue_rule():
+    """"auto" takes the fused gate/up kernel for at most 256 tokens whose
+    few-token tiles (128 tokens x 64 features) number at most one per
+    compute unit; the tile constants mirror the kernel's."""
+    import os
+    import re
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                             "mlp_gated_activation_amd", "csrc", "gemm_internal.h")).read()
+    tiles = re.search(r"kGemmTiles\[2\] = \{\{(\d+), (\d+)\}, \{(\d+), (\d+)\}\}", text)
+    assert (F._SMALL_TILE_TOKENS, F._SMALL_TILE_FEATURES) == (int(tiles.group(3)), int(tiles.group(4)))
+    assert F._SMALL_MAX_TOKENS == int(re.search(r"#define GLU_GEMM_SMALL_MAX_M (\d+)", text).group(1))
+    saved = dict(F._cu_count)
+    F._cu_count[0] = 256          # MI355X: 256 compute units (no device here)
+    try:
+        wins = lambda m, n: F.fused_epilogue_wins(m, n, "cuda:0")
+        assert wins(1, 14336) and wins(128, 14336) and not wins(129, 14336)    # 224, then 448 tiles
+        assert wins(256, 8192) and not wins(257, 8192)
+        assert not wins(16, 18944) and not wins(16, 28672)                     # 296, 448 tiles
+        assert wins(16, 64 * 256) and not wins(16, 64 * 256 + 1)
+        assert not wins(0, 8192)
+    finally:
+        F._cu_count.clear()
+        F._cu_count.update(saved)
