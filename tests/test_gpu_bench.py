@@ -46,3 +46,25 @@ def test_bench_op_prints_its_line(op):
                   "glu_strided": lambda a: a["tile_bwd_mix"]["GBps"]}[op](out["attainable"])
         assert 0 < attain < 8000
 
+
+def test_bench_gemm_shape_sweep():
+    """--gemm-shapes adds the fused / unfused comparison over other MLP shapes
+    and the path GatedMLP's default takes for each."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from conftest import ensure_built
+    ensure_built()
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--op", "gemm_glu", "--gemm-shapes", "--steps", "5",
+           "--warmup", "2", "--no-cpu-baseline"]
+    print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = json.loads([l for l in r.stdout.splitlines() if l.startswith("{")][-1])
+    sweep = out["shape_sweep"]
+    assert len(sweep) == 25
+    for row in sweep:
+        assert row["fused_us"] > 0 and row["unfused_us"] > 0
+        tiles = -(-row["M"] // 128) * -(-row["intermediate"] // 64)
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        assert row["auto_picks_fused"] == (row["M"] <= 256 and tiles <= ncu)
+
