@@ -126,6 +126,17 @@ def test_bf16_hidden_sweep(glu, name):
     _separate_fwd_bwd(glu, "silu", a, b, dy, w.name, bwd_out_of_place=False)
 
 
+@pytest.mark.parametrize("cols", [8184, 8192])
+def test_launch_shape_switch(glu, cols):
+    """Either side of 2^22 units (4096 x 8192 bf16), where the launcher
+    switches the backward from 512- to 128-thread blocks and starts capping
+    resident workgroups: fwd and bwd, in place and not, GELU-erf (the longest
+    arithmetic) and ReLU (bit-exact)."""
+    a, b, dy = inputs.separate(4096, cols, "bf16", 2.0, seed=7)
+    for kind in ("gelu_erf", "relu"):
+        _separate_fwd_bwd(glu, kind, a, b, dy, f"4096x{cols}")
+
+
 @pytest.fixture(scope="module")
 def stress_inputs():
     w = inputs.WORKLOADS["geglu_reglu_fp16_gateup_8191x18944"]
