@@ -88,13 +88,18 @@ template <bool PRECISE> __device__ inline double exp_neg(double a)
         p = __builtin_fma(p, r, c[i]);
     return __builtin_ldexp(p, int(k));
 }
-// 1/d for d >= 1: the hardware reciprocal and two Newton steps; each squares
-// the relative error, so even a seed within 2^-8 ends below 2^-32.
-__device__ inline double recip_ge1(double d)
+// 1/d for d >= 1: the hardware reciprocal, then Newton steps, each of which
+// squares the relative error.  The seed measured within 4.6e-8 (2^-24.4)
+// relative over d in [1, 128) on MI355X (2^24 points against the correctly
+// rounded quotient); the arguments here stay in [1, 24].  One step (the
+// forwards) leaves about 2^-48, two (PRECISE, the backward) fp64 rounding.
+template <bool PRECISE = true> __device__ inline double recip_ge1(double d)
 {
     double q = __builtin_amdgcn_rcp(d);
     q = __builtin_fma(q, __builtin_fma(-d, q, 1.0), q);
-    return __builtin_fma(q, __builtin_fma(-d, q, 1.0), q);
+    if constexpr (PRECISE)
+        q = __builtin_fma(q, __builtin_fma(-d, q, 1.0), q);
+    return q;
 }
 struct SigPartsD {
     double e, q;
@@ -102,7 +107,7 @@ struct SigPartsD {
 template <bool PRECISE = true> __device__ inline SigPartsD sig_parts(double a)
 {
     const double e = exp_neg<PRECISE>(a);
-    return SigPartsD{e, recip_ge1(1.0 + e)};
+    return SigPartsD{e, recip_ge1<PRECISE>(1.0 + e)};
 }
 
 constexpr double kInvSqrt2 = 0.70710678118654752440;      // [SWIGLU] reasoning step 7
@@ -163,9 +168,12 @@ __device__ inline double x_phi(double x, double h)
 // Phi(x) and phi(x) in fp64 for fp32 data, by the same substitution as
 // norm_cdf with fp64 tables, exp_neg and the reciprocal above.  PRECISE (the
 // backward): Q to 4.6e-10 relative, so Phi within about 5e-10 and phi within
-// a few fp64 ulps.  Otherwise (the forward): Q to 1.2e-8 and the shorter exp,
-// Phi within about 2e-8.  The forward x * Phi(x) has no cancellation, so
-// one rounding to fp32 keeps it well inside 1e-6; the backward's Phi + x phi
+// a few fp64 ulps.  Otherwise (the forward): Q to 1.7e-7 and the shorter exp
+// and reciprocal, Phi(-|x|) within about 1.8e-7.  The forward x * Phi(x)
+// carries that relative error (for x >= 0, x - |x| h with h <= 1/2 at most
+// doubles an absolute error of h that is itself at most half its relative
+// one), so with its one rounding to fp32 it stays below 2.5e-7, a quarter of
+// the 1e-6 bound; the backward's Phi + x phi
 // cancels near its root, where a Taylor expansion in fp64 takes over
 // (taylor_patch_d).  |x| is clamped to 64, beyond which Phi(-|x|) and phi
 // are 0 in fp64; NaN passes the clamp and makes h NaN.
@@ -175,7 +183,7 @@ template <bool PRECISE> __device__ inline double norm_tail_d(double x, double &E
     constexpr double cp[GLU_ERFC_QD_DEG + 1] = GLU_ERFC_QD_COEFFS;
     constexpr double cf[GLU_ERFC_QDF_DEG + 1] = GLU_ERFC_QDF_COEFFS;
     const double ax = fabs_(x) > 64.0 ? 64.0 : fabs_(x);
-    const double t = recip_ge1(__builtin_fma(ax, 0.5 * kInvSqrt2, 1.0));
+    const double t = recip_ge1<PRECISE>(__builtin_fma(ax, 0.5 * kInvSqrt2, 1.0));
     double q = PRECISE ? cp[deg] : cf[deg];
 #pragma unroll
     for (int k = deg - 1; k >= 0; --k)

@@ -39,7 +39,7 @@ def horner(coef, t):
 
 
 # the bound each table is held to by the kernels' error budgets
-BOUNDS = {"Q": 6.0e-7, "QF": 1.0e-4, "QD": 1.0e-9, "QDF": 5.0e-8}
+BOUNDS = {"Q": 6.0e-7, "QF": 1.0e-4, "QD": 1.0e-9, "QDF": 2.0e-7}
 
 
 @pytest.mark.parametrize("name", ["Q", "QF", "QD", "QDF"])
