@@ -172,13 +172,17 @@ template <typename M> __device__ inline M rsqrt_row(M ms, float eps) { return M(
 // (ragged vectors use a guarded, fully unrolled loop), so nothing is demoted
 // to scratch memory.  With 8 vectors per thread gamma is loaded in the
 // second phase (an L2 hit: every row reads the same gamma), halving the
-// registers held across the reduction.
-template <typename T, int BLOCK, int VPT, bool VEC>
+// registers held across the reduction -- unless GPACK, where its full
+// vectors are loaded with the row's first loads and held packed: more
+// registers (fewer waves per SIMD), but no wait on gamma between a row's
+// reduction and its y stores (rms_gamma_early picks between the two).
+template <typename T, int BLOCK, int VPT, bool VEC, bool GPACK = false>
 __global__ void __launch_bounds__(BLOCK) add_rmsnorm_kernel(const RmsArgs p)
 {
     using M = typename T::M;
     constexpr int VE = VEC ? T::VE : 1;
     constexpr bool G_EARLY = VPT <= 4;
+    constexpr bool G_PACK = GPACK && !G_EARLY && VEC;
     __shared__ M lds[BLOCK / 64];
     const int64_t row = blockIdx.x;
     const uint32_t H = p.hidden;
@@ -189,6 +193,7 @@ __global__ void __launch_bounds__(BLOCK) add_rmsnorm_kernel(const RmsArgs p)
 
     M h[VPT][VE];
     M g[G_EARLY ? VPT : 1][VE];
+    u32x4 gp[G_PACK ? VPT : 1];
     M ss = M(0);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
@@ -199,6 +204,8 @@ __global__ void __launch_bounds__(BLOCK) add_rmsnorm_kernel(const RmsArgs p)
             T::unpack(ldv<T>(rr, col), rv);
             if constexpr (G_EARLY)
                 T::unpack(ldv_cached<T>(p.gamma, col), g[v]);
+            if constexpr (G_PACK)
+                gp[v] = ldv_cached<T>(p.gamma, col);
 #pragma unroll
             for (int e = 0; e < VE; ++e) {
                 h[v][e] = xv[e] + rv[e];
@@ -232,6 +239,8 @@ __global__ void __launch_bounds__(BLOCK) add_rmsnorm_kernel(const RmsArgs p)
 #pragma unroll
                 for (int e = 0; e < T::VE; ++e)
                     gv[e] = g[v][e];
+            } else if constexpr (G_PACK) {
+                T::unpack(gp[v], gv);
             } else {
                 T::unpack(ldv_cached<T>(p.gamma, col), gv);
             }
@@ -456,6 +465,28 @@ template <typename T> RmsFn pick_rms_vec(bool vec, RmsShape s)
     return vec ? pick_rms<T, true>(s) : pick_rms<T, false>(s);
 }
 
+// Rows of the 64-thread, 8-vector shape one CU holds at once, four SIMDs
+// times the waves per SIMD its registers allow: <= 96 VGPRs (five waves)
+// with gamma loaded late, 97 .. 128 (four) with it early and packed.  The
+// kernel ISA test checks the compiled register counts against both.
+constexpr int64_t kRmsRowsPerCuLate = 20, kRmsRowsPerCuEarly = 16;
+
+// The early-gamma instance when it needs no more rounds of rows than the
+// late one.  bf16, 4096 wide, early against late, same process, bit-
+// identical: 4096 rows 23.99 / 23.93 us, 6144 38.1 / 41.3, 8192 48.6 /
+// 51.4, 12288 71.8 / 73.6, 16384 93.8 / 96.9 (and 8192 x 3072 37.2 /
+// 39.4), where both take the same number of rounds; but 5120 rows 33.5 /
+// 29.6, where the early one needs a second round.
+bool rms_gamma_early(uint32_t rows, hipStream_t stream)
+{
+    int dev = 0, cus = 0;
+    if ((stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return false;
+    const int64_t se = kRmsRowsPerCuEarly * cus, sl = kRmsRowsPerCuLate * cus;
+    return (int64_t(rows) + se - 1) / se == (int64_t(rows) + sl - 1) / sl;
+}
+
 }  // namespace
 
 hipError_t launch_add_rmsnorm(int dtype, bool vec, RmsShape shape, uint32_t rows, const RmsArgs &args,
@@ -478,6 +509,8 @@ hipError_t launch_add_rmsnorm(int dtype, bool vec, RmsShape shape, uint32_t rows
     RmsFn fn = dtype == F32 ? pick_rms_vec<RF32>(vec, shape)
              : dtype == F16 ? pick_rms_vec<RF16>(vec, shape)
                             : pick_rms_vec<RBf16>(vec, shape);
+    if (vec && dtype != F32 && shape.block == 64 && shape.vpt == 8 && rms_gamma_early(rows, stream))
+        fn = dtype == F16 ? &add_rmsnorm_kernel<RF16, 64, 8, true, true> : &add_rmsnorm_kernel<RBf16, 64, 8, true, true>;
     if (fn == nullptr)
         return hipErrorInvalidConfiguration;
     void *kargs[] = {&copy};

@@ -402,8 +402,18 @@ def test_rmsnorm_kernel_isa():
         asm = open(os.path.join(tmp, "rmsnorm_kernels-hip-amdgcn-amd-amdhsa-gfx950.s")).read()
     names = re.findall(r"^(_Z\w*rmsnorm\w*kernel\w*):", asm, re.M)
     # per dtype: 15 one-row shapes and the two-pass kernel, vector and element
-    # paths, and 5 pipelined multi-row shapes (vector path only)
-    assert len(names) == 3 * (2 * 16 + 5)
+    # paths, and 5 pipelined multi-row shapes (vector path only); for bf16 and
+    # fp16 also the 64 x 8 shape with gamma loaded early
+    assert len(names) == 3 * (2 * 16 + 5) + 2
+    # the rows per CU the launcher assumes for the 64 x 8 shape: five waves
+    # per SIMD (<= 96 VGPRs) with gamma late, four (97 .. 128) with it early
+    meta = {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"\.name:\s+(_Z\w+)\s*\n(?:\s+\.[^\n]*\n)*?\s+\.vgpr_count:\s+(\d+)", asm)}
+    for st in ("RBf16", "RF16"):
+        late = [v for n, v in meta.items() if re.search(rf"add_rmsnorm_kernelINS0_{len(st)}{st}ELi64ELi8ELb1ELb0E", n)]
+        early = [v for n, v in meta.items() if re.search(rf"add_rmsnorm_kernelINS0_{len(st)}{st}ELi64ELi8ELb1ELb1E", n)]
+        assert len(late) == 1 and len(early) == 1, (st, late, early)
+        assert late[0] <= 96 and 96 < early[0] <= 128, (st, late, early)
     # register arrays must stay in registers: no private (scratch) memory
     assert re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm) and \
         set(re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)) == {"0"}
@@ -413,5 +423,6 @@ def test_rmsnorm_kernel_isa():
         assert "mfma" not in body and not re.search(r"v_pk_(add|mul|fma)_f32", body), name
         if "RF32" not in name:
             assert not re.search(r"^\s+v_\w+_f64", body, re.M), name
-        if re.search(r"ELb1EEEvNS_7RmsArgsE", name) or "rows_kernel" in name:   # VEC instances
+        if (re.search(r"add_rmsnorm_kernelI\w+?ELi\d+ELi\d+ELb1ELb[01]E", name) or "rows_kernel" in name
+                or re.search(r"loop_kernelI\w+?ELb1EEEvNS_7RmsArgsE", name)):   # VEC instances
             assert "global_load_dwordx4" in body and "global_store_dwordx4" in body, name

@@ -56,6 +56,18 @@ def test_workload_bf16(glu, hidden):
     check_all(h, y, rstd, x, r, g, 1e-6, f"bf16 4096x{hidden}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("rows,hidden", [(5120, 4096), (6144, 4096), (8192, 3000)])
+def test_gamma_early_and_late(glu, dtype, rows, hidden):
+    """The 64-thread, 8-vector shape with gamma loaded late (5120 rows, where
+    the early-gamma instance would need a second round of rows on 256 CUs)
+    and early (6144 rows; 8192 x 3000, rows shorter than the shape's 4096)."""
+    x, r, g = inputs.add_rmsnorm(rows, hidden, dtype, seed=3)
+    gx, gr, gg = x.cuda(), r.cuda(), g.cuda()
+    h, y, rstd = glu.glu_add_rmsnorm_fwd(gx, gr, gg, 1e-6, rstd=True)
+    check_all(h, y, rstd, x, r, g, 1e-6, f"{dtype} {rows}x{hidden}")
+
+
 HIDDEN = [1, 7, 8, 100, 512, 513, 1024, 2048, 2049, 4096, 5120, 8192, 16384, 16385, 32768, 65536, 65544, 70000]
 
 
