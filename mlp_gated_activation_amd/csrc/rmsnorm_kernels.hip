@@ -471,12 +471,13 @@ template <typename T> RmsFn pick_rms_vec(bool vec, RmsShape s)
 // kernel ISA test checks the compiled register counts against both.
 constexpr int64_t kRmsRowsPerCuLate = 20, kRmsRowsPerCuEarly = 16;
 
-// The early-gamma instance when it needs no more rounds of rows than the
-// late one.  bf16, 4096 wide, early against late, same process, bit-
-// identical: 4096 rows 23.99 / 23.93 us, 6144 38.1 / 41.3, 8192 48.6 /
-// 51.4, 12288 71.8 / 73.6, 16384 93.8 / 96.9 (and 8192 x 3072 37.2 /
-// 39.4), where both take the same number of rounds; but 5120 rows 33.5 /
-// 29.6, where the early one needs a second round.
+// The early-gamma instance when the rows take more than one round of the
+// late one and no more rounds of the early one.  bf16, 4096 wide, early
+// against late, same process, bit-identical: 6144 rows 38.1 / 41.3 us, 8192
+// 48.6 / 51.4, 12288 71.8 / 73.6, 16384 93.8 / 96.9 (and 8192 x 3072 37.2 /
+// 39.4); within one round even (4096 rows 23.99 / 23.93), so the late one
+// stays there; and 5120 rows 33.5 / 29.6, where the early one needs a
+// second round.
 bool rms_gamma_early(uint32_t rows, hipStream_t stream)
 {
     int dev = 0, cus = 0;
@@ -484,7 +485,7 @@ bool rms_gamma_early(uint32_t rows, hipStream_t stream)
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return false;
     const int64_t se = kRmsRowsPerCuEarly * cus, sl = kRmsRowsPerCuLate * cus;
-    return (int64_t(rows) + se - 1) / se == (int64_t(rows) + sl - 1) / sl;
+    return int64_t(rows) > sl && (int64_t(rows) + se - 1) / se == (int64_t(rows) + sl - 1) / sl;
 }
 
 }  // namespace

@@ -57,7 +57,7 @@ def test_workload_bf16(glu, hidden):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("rows,hidden", [(5120, 4096), (6144, 4096), (8192, 3000)])
+@pytest.mark.parametrize("rows,hidden", [(5120, 4096), (6144, 4096), (8192, 3000), (16384, 4096)])
 def test_gamma_early_and_late(glu, dtype, rows, hidden):
     """The 64-thread, 8-vector shape with gamma loaded late (5120 rows, where
     the early-gamma instance would need a second round of rows on 256 CUs)
