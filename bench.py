@@ -210,7 +210,8 @@ def attainable(torch, stream, sets, n, restore):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", choices=["glu", "add_rmsnorm", "glu_strided", "gemm_glu", "providers", "mlp"], default="glu",
+    ap.add_argument("--op", choices=["glu", "add_rmsnorm", "glu_strided", "gemm_glu", "providers", "mlp", "configs"],
+                    default="glu",
                     help="glu: the SwiGLU fwd+bwd step (default); add_rmsnorm: the fused residual "
                          "add + RMSNorm forward, bf16, 4096 rows; glu_strided: the SwiGLU backward "
                          "with a transposed incoming gradient (LDS-tiled kernel) and related layouts; "
@@ -218,7 +219,8 @@ def main():
                          "(bf16, 4096 tokens, hidden 4096, I 14336); providers: the SwiGLU op at "
                          "4096 x H, H = 1024 .. 16384, against torch eager and torch.compile; mlp: a whole "
                          "SwiGLU MLP training step (4096 tokens, 4096 -> 14336, bf16), GatedMLP against the "
-                         "same network in torch, time and peak memory")
+                         "same network in torch, time and peak memory; configs: every workload configuration "
+                         "and kind, forward and backward per kernel")
     ap.add_argument("--hidden", type=int, default=4096, help="add_rmsnorm only: row width")
     ap.add_argument("--gemm-shapes", action="store_true",
                     help="gemm_glu only: also time the fused and unfused paths at 1 .. 256 tokens over other "
@@ -261,6 +263,8 @@ def main():
         return bench_providers(args, torch, glu, inputs, dev)
     if args.op == "mlp":
         return bench_mlp(args, torch, dev)
+    if args.op == "configs":
+        return bench_configs(args, torch, glu, inputs, dev)
     w = inputs.WORKLOADS["swiglu_bf16_4096x14336"]
     a_h, b_h, dy_h = w.make(seed=0)
     # pristine device copies of the operands the in-place backward overwrites
@@ -584,6 +588,90 @@ def bench_providers(args, torch, glu, inputs, dev):
     }
     if compile_error is not None:
         result["torch_compile_error"] = compile_error
+    print(json.dumps(result), flush=True)
+
+
+def bench_configs(args, torch, glu, inputs, dev):
+    """Every workload configuration, forward and backward per kernel through
+    the binding: the metric shape with all four kinds, the 11008-wide and
+    [gate | up] bf16 workloads, the hidden-size sweep and one TP = 8 rank's
+    share, the fp16 [gate | up] workload with rare large gate values for all
+    four kinds, and fp32 data (64 x 1024, and 4096 x 14336 with all four
+    kinds).  Every kernel is warmed up for at least 40 launches, then timed
+    over `--steps` (at most 60) launches rotating over at least 1.5 GB of
+    sets; the in-place backward's inputs are restored from pristine copies
+    between timed batches.  Calls go one by one through the binding, so the
+    smallest shapes (a few microseconds per call) show host-bound figures;
+    the providers op times them against HIP-graph replay.  Context: the
+    headline is the default op."""
+    stream = torch.cuda.current_stream(dev)
+    reps = max(1, min(args.steps, 60))
+    nothing = lambda: None
+    out = []
+
+    def time_kinds(name, layout, kinds, host):
+        """host: (a, b, dy) for separate, (x, dy) for gate_up, on the CPU."""
+        pristine = [t.to(dev) for t in host]
+        es = pristine[0].element_size()
+        R, C = pristine[-1].shape                      # dy is (rows, cols) in both layouts
+        nsets = max(2, -(-int(1.5e9) // (4 * R * C * es)))
+        sets = [[t.clone() for t in pristine] + [torch.empty(R, C, dtype=pristine[0].dtype, device=dev)]
+                for _ in range(nsets)]
+        nin = 2 if layout == "separate" else 1      # tensors the in-place backward overwrites
+
+        def restore():
+            for s_ in sets:
+                for j in range(nin):
+                    s_[j].copy_(pristine[j])
+        for kind in kinds:
+            if layout == "separate":
+                fwd = lambda i: glu.glu_fwd(kind, "separate", sets[i % nsets][0], sets[i % nsets][1],
+                                            sets[i % nsets][3])
+                bwd = lambda i: glu.glu_bwd(kind, "separate", sets[i % nsets][0], sets[i % nsets][1],
+                                            sets[i % nsets][2], inplace=True)
+            else:
+                fwd = lambda i: glu.glu_fwd(kind, "gate_up", sets[i % nsets][0], y=sets[i % nsets][2])
+                bwd = lambda i: glu.glu_bwd(kind, "gate_up", sets[i % nsets][0], None, sets[i % nsets][1],
+                                            inplace=True)
+            # warm-up: the clock settles to each kernel's load within tens of launches
+            warm = max(nsets, 40)
+            batched_ms(torch, stream, fwd, warm, nsets, nothing)
+            batched_ms(torch, stream, bwd, warm, nsets, restore)
+            t_f = batched_ms(torch, stream, fwd, reps, nsets, nothing) / reps
+            t_b = batched_ms(torch, stream, bwd, reps, nsets, restore) / reps
+            fb, bb = 3 * R * C * es, 5 * R * C * es
+            out.append({"workload": name, "kind": kind, "dtype": str(pristine[0].dtype).replace("torch.", ""),
+                        "layout": layout, "rows": R, "cols": C,
+                        "fwd_us": round(1e3 * t_f, 2), "fwd_GBps": round(fb / (t_f * 1e-3) / 1e9, 1),
+                        "bwd_us": round(1e3 * t_b, 2), "bwd_GBps": round(bb / (t_b * 1e-3) / 1e9, 1),
+                        "step_GBps": round((fb + bb) / ((t_f + t_b) * 1e-3) / 1e9, 1)})
+        del sets, pristine
+        torch.cuda.empty_cache()
+        print(f"configs: {name} done", file=sys.stderr, flush=True)
+
+    kinds4 = ["silu", "gelu_erf", "gelu_tanh", "relu"]
+    W = inputs.WORKLOADS
+    time_kinds("swiglu_bf16_4096x14336", "separate", kinds4, W["swiglu_bf16_4096x14336"].make(seed=0))
+    time_kinds("swiglu_bf16_4096x11008", "separate", ["silu"], W["swiglu_bf16_4096x11008"].make(seed=0))
+    time_kinds("swiglu_bf16_gateup_4096x14336", "gate_up", ["silu"], W["swiglu_bf16_gateup_4096x14336"].make(seed=0))
+    for name in [f"swiglu_bf16_4096x{h}" for h in (1024, 2048, 4096, 8192, 16384)] + ["swiglu_bf16_tp8_4096x1792"]:
+        time_kinds(name, "separate", ["silu"], W[name].make(seed=0))
+    time_kinds("geglu_reglu_fp16_gateup_8191x18944", "gate_up", kinds4,
+               W["geglu_reglu_fp16_gateup_8191x18944"].make(seed=0))
+    time_kinds("swiglu_f32_64x1024", "separate", ["silu"], W["swiglu_f32_64x1024"].make(seed=0))
+    time_kinds("fp32 4096x14336", "separate", kinds4, inputs.separate(4096, 14336, "fp32", 2.0, seed=0))
+    head = [r for r in out if r["workload"] == "swiglu_bf16_4096x14336" and r["kind"] == "silu"][0]
+    result = {
+        "metric": "achieved HBM GB/s per configuration, forward and backward per kernel (context)",
+        "value": head["step_GBps"], "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": round((head["fwd_us"] + head["bwd_us"]) * 1e-3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (value); every dtype in rows",
+        "data": "synthetic, the seeded workloads of mlp_gated_activation_amd.inputs; >= 1.5 GB of rotating "
+                "buffer sets per configuration; in-place inputs restored between timed batches",
+        "config": {"workload": "every configuration; value: SwiGLU bf16 (4096, 14336) fwd + bwd per kernel"},
+        "rows": out,
+        "cpu_baseline": None,
+    }
     print(json.dumps(result), flush=True)
 
 
