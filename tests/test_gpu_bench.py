@@ -19,7 +19,7 @@ KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "
         "vs_baseline", "dtype", "data", "config", "cpu_baseline"}
 
 
-@pytest.mark.parametrize("op", ["glu", "add_rmsnorm", "glu_strided", "gemm_glu", "mlp"])
+@pytest.mark.parametrize("op", ["glu", "add_rmsnorm", "glu_strided", "gemm_glu", "mlp", "configs"])
 def test_bench_op_prints_its_line(op):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -36,7 +36,9 @@ def test_bench_op_prints_its_line(op):
     assert KEYS <= set(out), sorted(KEYS - set(out))
     assert out["n_gpus"] == 1 and out["value"] and out["value"] > 0
     assert "workload" in out["config"]
-    if op != "mlp":
+    if op == "configs":
+        assert len(out["rows"]) == 21 and all(r["fwd_GBps"] > 0 and r["bwd_GBps"] > 0 for r in out["rows"])
+    elif op != "mlp":
         roof = out["roofline"]
         assert roof["peak"] > 0 and 0 < roof["frac"] < 1 and roof["bound"] in ("hbm", "mfma")
     if op in ("glu", "glu_strided", "add_rmsnorm"):
